@@ -1,0 +1,276 @@
+"""CPU oracle for the NVFP4 linear-layer path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never does, and
+this package imports nothing from the product.
+
+The quantizer, dequantizer and exact decode live in plain C
+(``nvfp4_oracle.c``, loaded with ctypes); the GEMM oracle is the plain
+definition written with a library matmul in float64:
+
+    C[m, n] = g_A * g_B * sum_k (q_A S_A)[m, k] * (q_B S_B)[n, k]
+
+where q*S is the exactly decoded element (an NVFP4 element times its E4M3
+block scale), g is the per-tensor FP32 decode scale, and the pages' source is
+the NVFP4 format description ([P4] aisight.pl "Koniec marnowania mocy ...",
+section "Architektura NVFP4 kontra ograniczenia mikroskalowania": 16-element
+blocks, E4M3 block scale, an FP32 tensor-level scale) together with the
+accelerated GEMM the format feeds ([P1] hyper.ai "NVIDIA revolutioniert
+KI-Praetrainingsgeschwindigkeit mit 4-Bit-Genauigkeit", body).
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+against worked examples, closed forms, library routines and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+RNE, SR = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (OpenMP, no FP contraction)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        c_i64, c_u64, c_u32, vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_value.restype = ctypes.c_float
+        L.oracle_e2m1_rne.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_rne.restype = ctypes.c_uint8
+        L.oracle_e2m1_sr.argtypes = [ctypes.c_float, c_u32]
+        L.oracle_e2m1_sr.restype = ctypes.c_uint8
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = ctypes.c_float
+        L.oracle_e4m3_rne_sat.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_rne_sat.restype = ctypes.c_uint8
+        L.oracle_philox4x32_10.argtypes = [vp, vp, vp]
+        L.oracle_philox4x32_10.restype = None
+        L.oracle_sr_bits.argtypes = [c_u64, c_u64, c_u64]
+        L.oracle_sr_bits.restype = c_u32
+        L.oracle_rht16.argtypes = [vp, c_u32, vp]
+        L.oracle_rht16.restype = None
+        L.oracle_quantize.argtypes = [vp, ctypes.c_int, c_i64, c_i64, ctypes.c_int,
+                                      ctypes.c_int, c_u64, c_u64, ctypes.c_int, c_u32,
+                                      vp, vp, vp]
+        L.oracle_quantize.restype = ctypes.c_int
+        L.oracle_dequantize.argtypes = [vp, vp, vp, c_i64, c_i64, ctypes.c_int, vp]
+        L.oracle_dequantize.restype = ctypes.c_int
+        L.oracle_decode_qs.argtypes = [vp, vp, c_i64, vp, c_i64, vp]
+        L.oracle_decode_qs.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+# --------------------------------------------------------------------------
+# scalar primitives
+# --------------------------------------------------------------------------
+
+def e2m1_value(code: int) -> float:
+    return float(lib().oracle_e2m1_value(code))
+
+
+def e2m1_rne(v: float) -> int:
+    return int(lib().oracle_e2m1_rne(v))
+
+
+def e2m1_sr(v: float, r16: int) -> int:
+    return int(lib().oracle_e2m1_sr(v, r16))
+
+
+def e4m3_value(b: int) -> float:
+    return float(lib().oracle_e4m3_value(b))
+
+
+def e4m3_rne_sat(t: float) -> int:
+    return int(lib().oracle_e4m3_rne_sat(t))
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32).reshape(2))
+    out = np.zeros(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_bits(seed: int, offset: int, i: int) -> int:
+    return int(lib().oracle_sr_bits(seed, offset, i))
+
+
+def rht16(x, sign_mask: int) -> np.ndarray:
+    xv = np.ascontiguousarray(np.asarray(x, dtype=np.float32).reshape(16))
+    y = np.zeros(16, dtype=np.float32)
+    lib().oracle_rht16(_ptr(xv), sign_mask & 0xFFFF, _ptr(y))
+    return y
+
+
+# --------------------------------------------------------------------------
+# tensors
+# --------------------------------------------------------------------------
+
+class Quantized:
+    """Oracle result: codes [outer][K/2] u8, scales [outer][K/16] u8, meta f32[2]."""
+
+    def __init__(self, codes, scales, meta, outer, k):
+        self.codes, self.scales, self.meta = codes, scales, meta
+        self.outer, self.k = outer, k
+
+    @property
+    def amax(self) -> float:
+        return float(self.meta[0])
+
+    @property
+    def g(self) -> float:
+        return float(self.meta[1])
+
+
+def _as_raw(x):
+    """Accept a numpy f32 array, a numpy uint16 array of bf16 bits, or a torch
+    CPU tensor (float32 / bfloat16).  Returns (array, dtype code)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            t = x.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16), BF16
+            if t.dtype == torch.float32:
+                return t.numpy(), F32
+            raise TypeError(f"unsupported dtype {t.dtype}")
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def quantize(x, axis: int = 1, rounding: int = RNE, seed: int = 0, offset: int = 0,
+             rht: bool = False, sign_mask: int = 0) -> Quantized:
+    a, dt = _as_raw(x)
+    a = np.ascontiguousarray(a)
+    rows, cols = a.shape
+    outer, K = (rows, cols) if axis else (cols, rows)
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    codes = np.zeros((outer, K // 2), dtype=np.uint8)
+    scales = np.zeros((outer, K // 16), dtype=np.uint8)
+    meta = np.zeros(2, dtype=np.float32)
+    rc = lib().oracle_quantize(_ptr(a), dt, rows, cols, axis, rounding, seed, offset,
+                               1 if rht else 0, sign_mask & 0xFFFF,
+                               _ptr(codes), _ptr(scales), _ptr(meta))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize failed: {rc}")
+    return Quantized(codes, scales, meta, outer, K)
+
+
+def dequantize(q: Quantized, y_dtype: int = F32) -> np.ndarray:
+    out = np.zeros((q.outer, q.k), dtype=np.float32 if y_dtype == F32 else np.uint16)
+    rc = lib().oracle_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.meta),
+                                 q.outer, q.k, y_dtype, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_dequantize failed: {rc}")
+    return out
+
+
+def decode_qs(q: Quantized, rows=None) -> np.ndarray:
+    """Exact q*S (without g) for the selected outer rows, float64 [n][K]."""
+    if rows is None:
+        rows = np.arange(q.outer, dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.zeros((rows.size, q.k), dtype=np.float64)
+    rc = lib().oracle_decode_qs(_ptr(q.codes), _ptr(q.scales), q.k, _ptr(rows),
+                                rows.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_qs failed: {rc}")
+    return out
+
+
+def gemm(qa: Quantized, qb: Quantized, rows=None, cols=None):
+    """GEMM oracle C = A B^T on the NVFP4 operands, float64.
+
+    Returns (C, bound) restricted to the selected rows of A (outer index m)
+    and rows of B (outer index n).  bound = g_A g_B sum_k |(qS)_A (qS)_B|, the
+    scale the tolerance 1e-5 * bound is taken against.
+    """
+    if qa.k != qb.k:
+        raise ValueError("K mismatch")
+    da = decode_qs(qa, rows)
+    db = decode_qs(qb, cols)
+    gg = float(np.float64(qa.meta[1]) * np.float64(qb.meta[1]))
+    c = (da @ db.T) * gg
+    bound = (np.abs(da) @ np.abs(db).T) * abs(gg)
+    return c, bound
+
+
+def check_gemm_f32(c_gpu: np.ndarray, c_ref: np.ndarray, bound: np.ndarray,
+                   rtol: float = 1e-5):
+    """Tolerance rule for f32 output: |C - Cref| <= rtol * bound elementwise
+    (bound == 0 requires C == 0 exactly).  Returns (ok, worst ratio)."""
+    c = np.asarray(c_gpu, dtype=np.float64)
+    err = np.abs(c - c_ref)
+    lim = rtol * bound
+    ok = bool(np.all(err <= lim))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    return ok, float(np.max(ratio)) if ratio.size else 0.0
+
+
+def _bf16_rne_of_f64(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (nearest even) via f32; returns float64.
+
+    Used only with values whose f32 rounding cannot change the bf16 result
+    interval test (the interval ends are rounded the same way)."""
+    import torch
+    t = torch.from_numpy(np.asarray(x, dtype=np.float64)).to(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def check_gemm_bf16(c_gpu_bf16_as_f64: np.ndarray, c_ref: np.ndarray, bound: np.ndarray,
+                    rtol: float = 1e-5):
+    """Tolerance rule for bf16 output: bf16(Cref - rtol*bound) <= C <=
+    bf16(Cref + rtol*bound) (rounding is monotone)."""
+    lo = _bf16_rne_of_f64(c_ref - rtol * bound)
+    hi = _bf16_rne_of_f64(c_ref + rtol * bound)
+    c = np.asarray(c_gpu_bf16_as_f64, dtype=np.float64)
+    ok = bool(np.all((c >= lo) & (c <= hi)))
+    return ok, int(np.sum(~((c >= lo) & (c <= hi))))
