@@ -1,0 +1,178 @@
+"""Python binding of the MI355X NVFP4 linear-layer library (``libnvfp4.so``).
+
+Argument marshalling only: every step of quantize / dequantize / GEMM runs in
+the gfx950 kernels behind the C ABI of ``include/nvfp4.h``.  torch supplies
+device memory and the current HIP stream.  There is no CPU fallback: if the
+library is not built, or no GPU is visible, the calls raise.
+
+Names follow the C ABI: ``nvfp4_quantize``, ``nvfp4_rht_quantize``,
+``nvfp4_dequantize``, ``nvfp4_gemm``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize",
+           "nvfp4_dequantize", "nvfp4_gemm", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+F32, BF16 = 0, 1
+RNE, SR = 0, 1
+
+
+class NVFP4Error(RuntimeError):
+    pass
+
+
+class _CTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("outer", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+_lib = None
+
+# every symbol the header declares
+EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize", "nvfp4_gemm",
+           "nvfp4_status_string")
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libnvfp4.so`` (build it with ``gemm_amax_reduce_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise NVFP4Error(f"{LIB_PATH} is missing: run gemm_amax_reduce_amd/build.py "
+                             "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, u64, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int
+        pt = ctypes.POINTER(_CTensor)
+        L.nvfp4_quantize.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, pt, vp]
+        L.nvfp4_quantize.restype = ci
+        L.nvfp4_rht_quantize.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, ctypes.c_uint16, pt, vp]
+        L.nvfp4_rht_quantize.restype = ci
+        L.nvfp4_dequantize.argtypes = [pt, vp, ci, vp]
+        L.nvfp4_dequantize.restype = ci
+        L.nvfp4_gemm.argtypes = [pt, pt, vp, ci, i64, vp]
+        L.nvfp4_gemm.restype = ci
+        L.nvfp4_status_string.argtypes = [ci]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = lib().nvfp4_status_string(rc).decode()
+        raise NVFP4Error(f"{what} failed: {msg} ({rc})")
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _require_device(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise NVFP4Error(f"{name} must be a GPU tensor (no CPU path exists)")
+
+
+class NVFP4Tensor:
+    """Device buffers of one NVFP4 tensor in its quantized [outer][k] layout:
+    ``codes`` u8 [outer, k/2], ``scales`` u8 [outer, k/16], ``meta`` f32 [2]
+    = (amax, g)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, meta: torch.Tensor, outer: int, k: int):
+        self.codes, self.scales, self.meta = codes, scales, meta
+        self.outer, self.k = int(outer), int(k)
+
+    @classmethod
+    def empty(cls, outer: int, k: int, device=None) -> "NVFP4Tensor":
+        device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        codes = torch.empty((outer, k // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((outer, k // 16), dtype=torch.uint8, device=device)
+        meta = torch.empty(2, dtype=torch.float32, device=device)
+        return cls(codes, scales, meta, outer, k)
+
+    def _c(self) -> _CTensor:
+        return _CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.meta.data_ptr(), self.outer, self.k)
+
+    @property
+    def shape(self):
+        return (self.outer, self.k)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise NVFP4Error(f"unsupported input dtype {t.dtype} (f32 or bf16)")
+
+
+def _rounding_code(r) -> int:
+    if isinstance(r, str):
+        r = {"rne": RNE, "sr": SR}[r.lower()]
+    return int(r)
+
+
+def _quantize(x, axis, rounding, seed, offset, rht, sign_mask, out, stream):
+    _require_device(x, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise NVFP4Error("x must be a contiguous 2-D tensor")
+    rows, cols = x.shape
+    outer, k = (rows, cols) if axis == 1 else (cols, rows)
+    if out is None:
+        out = NVFP4Tensor.empty(outer, k, device=x.device)
+    ct = out._c()
+    if rht:
+        rc = lib().nvfp4_rht_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding),
+                                      seed, offset, sign_mask & 0xFFFF, ctypes.byref(ct), _stream_handle(stream))
+    else:
+        rc = lib().nvfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding),
+                                  seed, offset, ctypes.byref(ct), _stream_handle(stream))
+    _check(rc, "nvfp4_rht_quantize" if rht else "nvfp4_quantize")
+    return out
+
+
+def nvfp4_quantize(x: torch.Tensor, axis: int = 1, rounding="rne", seed: int = 0, offset: int = 0,
+                   out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """Quantize a 2-D f32/bf16 GPU tensor to NVFP4 (see include/nvfp4.h)."""
+    return _quantize(x, axis, rounding, seed, offset, False, 0, out, stream)
+
+
+def nvfp4_rht_quantize(x: torch.Tensor, sign_mask: int, axis: int = 1, rounding="rne", seed: int = 0,
+                       offset: int = 0, out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """Quantize after the 16-point random Hadamard transform along k."""
+    return _quantize(x, axis, rounding, seed, offset, True, sign_mask, out, stream)
+
+
+def nvfp4_dequantize(q: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Decode to f32/bf16 in the quantized [outer][k] layout."""
+    code = F32 if dtype == torch.float32 else BF16
+    if out is None:
+        out = torch.empty((q.outer, q.k), dtype=dtype, device=q.codes.device)
+    ct = q._c()
+    _check(lib().nvfp4_dequantize(ctypes.byref(ct), out.data_ptr(), code, _stream_handle(stream)),
+           "nvfp4_dequantize")
+    return out
+
+
+def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """C = A . B^T for A [M, K] and B [N, K] NVFP4 tensors, f32 accumulation."""
+    code = F32 if out_dtype == torch.float32 else BF16
+    if out is None:
+        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=a.codes.device)
+    if out.dim() != 2 or out.stride(1) != 1:
+        raise NVFP4Error("out must be a row-major 2-D tensor")
+    ldc = out.stride(0) if out.shape[0] > 1 else max(out.shape[1], 1)
+    ca, cb = a._c(), b._c()
+    _check(lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
+                            _stream_handle(stream)), "nvfp4_gemm")
+    return out

@@ -1,0 +1,93 @@
+// api.hip -- the extern "C" boundary declared in include/nvfp4.h: argument
+// validation (synchronous, before any launch) and kernel launches on the
+// caller's stream.  Nothing here allocates or synchronises.
+#include "nvfp4.h"
+#include "nvfp4_kernels.h"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+int check_tensor(const nvfp4_tensor *t) {
+  if (!t || !t->meta) return NVFP4_ERR_NULL;
+  if (t->outer < 0 || t->k < 0 || t->k % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (t->outer > 0 && t->k > 0 && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
+  if (!aligned(t->codes, 8) || !aligned(t->meta, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+int quantize_common(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                    uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, nvfp4_tensor *out,
+                    void *hip_stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_ENUM;
+  if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  const int64_t outer = axis ? rows : cols;
+  const int64_t k = axis ? cols : rows;
+  if (k % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
+  int st = check_tensor(out);
+  if (st != NVFP4_OK) return st;
+  if (!aligned(x, 16)) return NVFP4_ERR_ALIGN;
+  hipError_t e = nvfp4::launch_quantize(x, x_dtype, rows, cols, axis, rounding, seed, offset, rht, sign_mask,
+                                        out->codes, out->scales, out->meta, (hipStream_t)hip_stream);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding, uint64_t seed,
+                   uint64_t offset, nvfp4_tensor *out, void *hip_stream) {
+  return quantize_common(x, x_dtype, rows, cols, axis, rounding, seed, offset, false, 0u, out, hip_stream);
+}
+
+int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                       uint64_t seed, uint64_t offset, uint16_t sign_mask, nvfp4_tensor *out, void *hip_stream) {
+  return quantize_common(x, x_dtype, rows, cols, axis, rounding, seed, offset, true, sign_mask, out, hip_stream);
+}
+
+int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stream) {
+  int st = check_tensor(q);
+  if (st != NVFP4_OK) return st;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (q->outer > 0 && q->k > 0 && !y) return NVFP4_ERR_NULL;
+  if (!aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_dequantize(q->codes, q->scales, q->meta, q->outer, q->k, y, y_dtype,
+                                              (hipStream_t)hip_stream));
+}
+
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc, void *hip_stream) {
+  int st = check_tensor(a);
+  if (st != NVFP4_OK) return st;
+  st = check_tensor(b);
+  if (st != NVFP4_OK) return st;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (a->k != b->k) return NVFP4_ERR_SHAPE;
+  const int64_t M = a->outer, N = b->outer;
+  if (ldc < N || ldc < 0) return NVFP4_ERR_SHAPE;
+  if (M > 0 && N > 0 && !c) return NVFP4_ERR_NULL;
+  if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_gemm(a->codes, a->scales, a->meta, b->codes, b->scales, b->meta, M, N, a->k, c,
+                                       c_dtype, ldc, (hipStream_t)hip_stream));
+}
+
+const char *nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "null pointer";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_ENUM: return "invalid enum value";
+    case NVFP4_ERR_HIP: return "HIP launch failed";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

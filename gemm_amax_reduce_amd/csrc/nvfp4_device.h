@@ -1,0 +1,235 @@
+// nvfp4_device.h -- gfx950 device helpers for the NVFP4 kernels.
+//
+// Format ([P4] aisight.pl "Koniec marnowania mocy ...", section "Architektura
+// NVFP4 kontra ograniczenia mikroskalowania"): 4-bit E2M1 elements, one
+// E4M3 scale per 16 elements along the reduction dimension, one FP32 scale
+// per tensor.  Every helper here is written for CDNA4 and relies on three
+// measured properties of gfx950:
+//  * v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds binary32 to E2M1
+//    nearest-even (ties to the even code), saturates at 6 and keeps the sign
+//    of zero;
+//  * v_cvt_scalef32_pk_f16_fp4 with scale 1.0 decodes E2M1 exactly (its scale
+//    operand only contributes its exponent, so the E4M3 block scale is
+//    applied with a separate exact f16 multiply);
+//  * v_cvt_f32_fp8 decodes OCP E4M3FN, binary32 denormals are kept and
+//    __fdiv_rn is the correctly rounded quotient.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
+// Tensor-level constants: 2688 = 6 * 448 maps the tensor maximum onto the
+// largest element (6) times the largest block scale (448).
+constexpr float kTensorRange = 2688.0f;
+constexpr float kScaleMax = 448.0f;
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Load 16 consecutive elements (bf16 or f32) starting at p (16-byte aligned)
+// as binary32 values.
+template <typename T> struct Load16;
+template <> struct Load16<uint16_t> {
+  __device__ __forceinline__ static void run(const uint16_t *p, float *y) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    uint4 a = q[0], b = q[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { y[2 * i] = bf16_lo(w[i]); y[2 * i + 1] = bf16_hi(w[i]); }
+  }
+};
+template <> struct Load16<float> {
+  __device__ __forceinline__ static void run(const float *p, float *y) {
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 v = q[i];
+      y[4 * i] = v.x; y[4 * i + 1] = v.y; y[4 * i + 2] = v.z; y[4 * i + 3] = v.w;
+    }
+  }
+};
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+
+// ---------------------------------------------------------------- E4M3 ----
+// Nearest-even E4M3FN code of t >= 0, saturating at 448.  Below 2^-6 the
+// code is the count of 2^-9 steps: adding 2^14 (whose ulp is 2^-9) rounds t
+// to that grid in one IEEE addition.  From 2^-6 up the binary32 pattern is
+// rounded to three mantissa bits and the exponent is rebiased (127 -> 7).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
+  t = fminf(t, kScaleMax);
+  if (t < 0x1p-6f) {
+    float s = t + 16384.0f;
+    return __float_as_uint(s) - 0x46800000u;  // 0x46800000 = bits of 2^14
+  }
+  uint32_t u = __float_as_uint(t);
+  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  return (r >> 20) - (120u << 3);
+}
+
+// E4M3FN code (0..0x7E) to binary32 (hardware OCP decode, exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+}
+
+// ---------------------------------------------------------------- E2M1 ----
+// Two binary32 values to two E2M1 codes (nearest-even, saturating, sign of
+// zero kept), written into byte `sel` of `old` (low nibble = first value).
+#define NVFP4_PK_FP4(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
+
+// Encode 8 values into one 32-bit word of nibbles (element 0 lowest).
+__device__ __forceinline__ uint32_t encode8_rne(const float *v) {
+  uint32_t w = 0;
+  w = NVFP4_PK_FP4(w, v[0], v[1], 0);
+  w = NVFP4_PK_FP4(w, v[2], v[3], 1);
+  w = NVFP4_PK_FP4(w, v[4], v[5], 2);
+  w = NVFP4_PK_FP4(w, v[6], v[7], 3);
+  return w;
+}
+
+// Stochastic rounding of one value with 16 random bits r16: with lo the
+// largest grid magnitude <= |v| and frac the position between lo and the
+// next grid point, round up iff r16 < frac * 2^16 ([P4] "Technologie
+// stabilizujace ...": stochastic rounding removes the systematic error).
+// The binade of |v| picks the grid spacing (0.5 below 2, 1 in [2,4), 2 in
+// [4,6)); scaling by its inverse (an exact power of two) turns the grid into
+// the integers, so floor and the remainder are exact.
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t r16) {
+  uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  float a = __builtin_fabsf(v);
+  uint32_t e = __float_as_uint(a) >> 23;
+  uint32_t c = min(max(e, 127u), 129u);           // 127: a<2, 128: [2,4), 129: >=4
+  float inv_step = __uint_as_float((255u - c) << 23);  // 2, 1, 0.5
+  float t = a * inv_step;
+  float f = __builtin_floorf(t);
+  float frac = t - f;
+  uint32_t up = ((float)r16 < frac * 65536.0f) ? 1u : 0u;
+  uint32_t code = (uint32_t)f + up + 2u * (c - 127u);
+  code = (a < 6.0f) ? code : 7u;                  // saturation (and NaN -> 7)
+  return sign | code;
+}
+
+// -------------------------------------------------------------- Philox ----
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64 products
+// with the multipliers 0xD2511F53 / 0xCD9E8D57, word permutation, and a key
+// schedule bumped by the Weyl constants 0x9E3779B9 / 0xBB67AE85.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+    uint32_t lo0 = 0xD2511F53u * c.x;
+    uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+    uint32_t lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// 16-bit random values for the 8 elements with output indices 8g .. 8g+7:
+// counter (lo(g), hi(g), lo(offset), hi(offset)), key (lo(seed), hi(seed));
+// element 8g+j takes half (j & 1) (low first) of word j >> 1.
+__device__ __forceinline__ void sr_bits8(uint64_t g, uint64_t seed, uint64_t offset, uint32_t *r) {
+  uint4 w = philox4x32_10(make_uint4((uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset,
+                                     (uint32_t)(offset >> 32)),
+                          (uint32_t)seed, (uint32_t)(seed >> 32));
+  r[0] = w.x & 0xFFFFu; r[1] = w.x >> 16;
+  r[2] = w.y & 0xFFFFu; r[3] = w.y >> 16;
+  r[4] = w.z & 0xFFFFu; r[5] = w.z >> 16;
+  r[6] = w.w & 0xFFFFu; r[7] = w.w >> 16;
+}
+
+// ----------------------------------------------------------------- RHT ----
+// 16-point random Hadamard transform in registers ([P4] "Technologie
+// stabilizujace ..."): sign flips from the mask, the Walsh-Hadamard
+// butterfly with stages 1, 2, 4, 8 (lower index a+b, upper a-b), then the
+// exact factor 1/4.
+__device__ __forceinline__ void rht16(float *t, uint32_t sign_mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    t[j] = ((sign_mask >> j) & 1u) ? -t[j] : t[j];
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j & h) continue;
+      float a = t[j], b = t[j + h];
+      t[j] = a + b;
+      t[j + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] = 0.25f * t[j];
+}
+
+// Largest |value| of 16 binary32 values as a bit pattern (exact, NaN > Inf).
+__device__ __forceinline__ uint32_t absmax_bits16(const float *y) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(y[j]) & 0x7FFFFFFFu);
+  return m;
+}
+
+// ------------------------------------------------------ tensor scales ----
+struct TensorScales {
+  float s_enc;  // 2688 / amax
+  float k;      // 448 / amax (block maxima -> E4M3 scale)
+  float g;      // amax / 2688 (decode)
+};
+
+__device__ __forceinline__ TensorScales tensor_scales(float amax) {
+  TensorScales s;
+  if (amax == 0.0f) {
+    s.s_enc = 0.0f; s.k = 0.0f; s.g = 0.0f;
+  } else {
+    s.s_enc = __fdiv_rn(kTensorRange, amax);
+    s.k = __fdiv_rn(kScaleMax, amax);
+    s.g = __fdiv_rn(amax, kTensorRange);
+  }
+  return s;
+}
+
+// Block scale code and element multiplier of one 16-block.
+__device__ __forceinline__ uint32_t block_scale(uint32_t bmax_bits, const TensorScales &ts, float *m) {
+  uint32_t S = e4m3_rne_sat(__uint_as_float(bmax_bits) * ts.k);
+  *m = (S == 0u) ? 0.0f : __fdiv_rn(ts.s_enc, e4m3_to_f32(S));
+  return S;
+}
+
+// Quantize 16 values with their multiplier m; returns the 8 code bytes as
+// two words.  RNE uses the hardware conversion, SR the Philox bits of the
+// block (output indices 16*blk .. 16*blk+15 have counters 2*blk and 2*blk+1).
+template <bool SR>
+__device__ __forceinline__ uint2 encode16(const float *y, float m, uint64_t blk, uint64_t seed,
+                                          uint64_t offset) {
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = y[j] * m;
+  if (!SR) {
+    return make_uint2(encode8_rne(v), encode8_rne(v + 8));
+  } else {
+    uint32_t r[16];
+    sr_bits8(2 * blk, seed, offset, r);
+    sr_bits8(2 * blk + 1, seed, offset, r + 8);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      w0 |= e2m1_sr(v[j], r[j]) << (4 * j);
+      w1 |= e2m1_sr(v[8 + j], r[8 + j]) << (4 * j);
+    }
+    return make_uint2(w0, w1);
+  }
+}
+
+}  // namespace nvfp4

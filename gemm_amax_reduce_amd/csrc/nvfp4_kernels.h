@@ -1,0 +1,26 @@
+// nvfp4_kernels.h -- host-side launch entry points of the gfx950 kernels
+// (internal to the library; the public C ABI is include/nvfp4.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kQuantThreads = 256;
+
+// Enqueue meta reset, amax and encode for one quantization.  Arguments are
+// validated by the caller; x_dtype 0 = f32, 1 = bf16; rounding 0 = RNE,
+// 1 = SR; rht selects the fused Hadamard transform.
+hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                           uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
+                           uint8_t *scales, float *meta, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *meta, int64_t outer,
+                             int64_t k, void *y, int y_dtype, hipStream_t stream);
+
+// C[M][ldc] = gA gB * A (M x K) . B^T (N x K); out_dtype 0 = f32, 1 = bf16.
+hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_meta,
+                       const uint8_t *b_codes, const uint8_t *b_scales, const float *b_meta, int64_t M,
+                       int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,277 @@
+// quantize.hip -- NVFP4 quantizer kernels for gfx950: tensor amax,
+// block-scaled E2M1 encode (nearest-even or Philox stochastic rounding),
+// optional fused 16-point random Hadamard transform, and dequantize.
+//
+// Format and recipe: [P4] aisight.pl "Koniec marnowania mocy ...", sections
+// "Architektura NVFP4 kontra ograniczenia mikroskalowania" (16-element
+// blocks, E4M3 block scale, FP32 tensor scale) and "Technologie
+// stabilizujace proces treningowy" (random Hadamard transform, stochastic
+// rounding); [P3] aibuzzwire.news "End-to-End 4-Bit Training" article,
+// section "Warum weniger Bits ein schnelleres Training bedeuten" (rounding to
+// the nearest representable value).
+//
+// Pass structure: the per-tensor scale needs the whole-tensor maximum before
+// any block can be encoded, so a quantization is (1) a one-thread kernel that
+// zeroes meta, (2) an amax kernel (integer max of |x| bit patterns, wave
+// reduction, one atomicMax per workgroup), (3) the encode kernel, which
+// re-reads the input.  Both data kernels stream the input with 16-byte loads.
+#include "nvfp4_device.h"
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+
+// ------------------------------------------------------------- helpers ----
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Reduce a per-thread max over the workgroup and fold it into *dst.
+__device__ __forceinline__ void block_max_atomic(uint32_t v, uint32_t *dst) {
+  __shared__ uint32_t part[kQuantThreads / 64];
+  v = wave_max(v);
+  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = part[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / 64; ++i) m = max(m, part[i]);
+    if (m) atomicMax(dst, m);
+  }
+}
+
+__global__ void k_meta_init(float *meta) {
+  if (threadIdx.x == 0) {
+    meta[0] = 0.0f;
+    meta[1] = 0.0f;
+  }
+}
+
+// --------------------------------------------------------------- amax ----
+
+// Flat amax over n16 16-byte vectors (no transform; the axis does not matter).
+template <typename T>
+__global__ void __launch_bounds__(kQuantThreads) k_amax_flat(const uint4 *x, int64_t n16, uint32_t *amax_bits) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n16; i += stride) {
+    uint4 v = x[i];
+    if constexpr (sizeof(T) == 2) {
+      ushort2_t acc = __builtin_bit_cast(ushort2_t, v.x & 0x7FFF7FFFu);
+      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(ushort2_t, v.y & 0x7FFF7FFFu));
+      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(ushort2_t, v.z & 0x7FFF7FFFu));
+      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(ushort2_t, v.w & 0x7FFF7FFFu));
+      m = max(m, (uint32_t)max(acc.x, acc.y) << 16);
+    } else {
+      m = max(m, v.x & 0x7FFFFFFFu);
+      m = max(m, v.y & 0x7FFFFFFFu);
+      m = max(m, v.z & 0x7FFFFFFFu);
+      m = max(m, v.w & 0x7FFFFFFFu);
+    }
+  }
+  block_max_atomic(m, amax_bits);
+}
+
+// amax of the transformed tensor, axis 1: one thread per 16-chunk of a row.
+template <typename T>
+__global__ void __launch_bounds__(kQuantThreads) k_amax_rht_rows(const T *x, int64_t nchunks, uint32_t sign_mask,
+                                                                uint32_t *amax_bits) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; c < nchunks; c += stride) {
+    float y[16];
+    Load16<T>::run(x + 16 * c, y);
+    rht16(y, sign_mask);
+    m = max(m, absmax_bits16(y));
+  }
+  block_max_atomic(m, amax_bits);
+}
+
+// Column-block loader for axis 0: 16 rows (one K block) of the column `col`.
+template <typename T>
+__device__ __forceinline__ void load_col16(const T *x, int64_t cols, int64_t r0, int64_t col, float *y) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(x[(r0 + j) * cols + col]);
+}
+
+// amax of the transformed tensor, axis 0: one thread per (K block, column).
+// Consecutive threads take consecutive columns so each row read is coalesced.
+template <typename T>
+__global__ void __launch_bounds__(kQuantThreads) k_amax_rht_cols(const T *x, int64_t rows, int64_t cols,
+                                                                uint32_t sign_mask, uint32_t *amax_bits) {
+  uint32_t m = 0;
+  const int64_t nunits = (rows / 16) * cols;
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t u = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; u < nunits; u += stride) {
+    int64_t kb = u / cols, col = u - kb * cols;
+    float y[16];
+    load_col16<T>(x, cols, 16 * kb, col, y);
+    rht16(y, sign_mask);
+    m = max(m, absmax_bits16(y));
+  }
+  block_max_atomic(m, amax_bits);
+}
+
+// ------------------------------------------------------------- encode ----
+
+// axis 1: one thread per 16-block (o, b); codes are 8 contiguous bytes.
+template <typename T, bool SR, bool RHT>
+__global__ void __launch_bounds__(kQuantThreads) k_quant_rows(const T *x, int64_t nblocks, uint32_t sign_mask,
+                                                             uint64_t seed, uint64_t offset, float *meta,
+                                                             uint2 *codes, uint8_t *scales) {
+  const float amax = meta[0];
+  const TensorScales ts = tensor_scales(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) meta[1] = ts.g;
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblocks; b += stride) {
+    float y[16];
+    Load16<T>::run(x + 16 * b, y);
+    if (RHT) rht16(y, sign_mask);
+    float m;
+    uint32_t S = block_scale(absmax_bits16(y), ts, &m);
+    codes[b] = encode16<SR>(y, m, (uint64_t)b, seed, offset);
+    scales[b] = (uint8_t)S;
+  }
+}
+
+// axis 0: one thread per (K block kb, column o); output row o, block kb.
+template <typename T, bool SR, bool RHT>
+__global__ void __launch_bounds__(kQuantThreads) k_quant_cols(const T *x, int64_t rows, int64_t cols,
+                                                             uint32_t sign_mask, uint64_t seed, uint64_t offset,
+                                                             float *meta, uint2 *codes, uint8_t *scales) {
+  const float amax = meta[0];
+  const TensorScales ts = tensor_scales(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) meta[1] = ts.g;
+  const int64_t nkb = rows / 16;
+  const int64_t nunits = nkb * cols;
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t u = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; u < nunits; u += stride) {
+    int64_t kb = u / cols, o = u - kb * cols;
+    float y[16];
+    load_col16<T>(x, cols, 16 * kb, o, y);
+    if (RHT) rht16(y, sign_mask);
+    float m;
+    uint32_t S = block_scale(absmax_bits16(y), ts, &m);
+    const int64_t blk = o * nkb + kb;  // block index in the [outer][K/16] layout
+    codes[blk] = encode16<SR>(y, m, (uint64_t)blk, seed, offset);
+    scales[blk] = (uint8_t)S;
+  }
+}
+
+// ---------------------------------------------------------- dequantize ----
+
+// One thread per 16-block: value = (e2m1 * S) * g, S applied exactly in f16.
+template <typename TO>
+__global__ void __launch_bounds__(kQuantThreads) k_dequant(const uint2 *codes, const uint8_t *scales,
+                                                          const float *meta, int64_t nblocks, TO *y) {
+  const float g = meta[1];
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblocks; b += stride) {
+    uint2 c = codes[b];
+    float S = e4m3_to_f32(scales[b]);
+    float v[16];
+    uint32_t w[2] = {c.x, c.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t nib = (w[h] >> (4 * j)) & 15u;
+        half2_t q = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 0);
+        v[8 * h + j] = ((float)q[0] * S) * g;
+      }
+    }
+    if constexpr (sizeof(TO) == 4) {
+      float4 *dst = reinterpret_cast<float4 *>(y + 16 * b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    } else {
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // nearest-even bf16 of each f32 (NaN cannot occur for finite meta)
+        uint32_t lo = __float_as_uint(v[2 * i]), hi = __float_as_uint(v[2 * i + 1]);
+        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+        o[i] = lo | (hi << 16);
+      }
+      uint4 *dst = reinterpret_cast<uint4 *>(y + 16 * b);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+// ------------------------------------------------------------ launches ----
+
+static inline unsigned grid_for(int64_t work, int64_t per_block = kQuantThreads, int64_t cap = 1 << 20) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                           uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
+                           uint8_t *scales, float *meta, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  uint32_t *amax_bits = reinterpret_cast<uint32_t *>(meta);
+  hipLaunchKernelGGL(k_meta_init, dim3(1), dim3(64), 0, stream, meta);
+  if (n == 0) return hipGetLastError();
+  const bool bf16 = (x_dtype == 1);
+  // pass 1: amax
+  if (!rht) {
+    const int64_t n16 = n * (bf16 ? 2 : 4) / 16;
+    unsigned g = grid_for(n16, kQuantThreads * 8, 2048);
+    if (bf16) hipLaunchKernelGGL(k_amax_flat<uint16_t>, dim3(g), dim3(kQuantThreads), 0, stream, (const uint4 *)x, n16, amax_bits);
+    else hipLaunchKernelGGL(k_amax_flat<float>, dim3(g), dim3(kQuantThreads), 0, stream, (const uint4 *)x, n16, amax_bits);
+  } else if (axis == 1) {
+    const int64_t nch = n / 16;
+    unsigned g = grid_for(nch, kQuantThreads * 4, 4096);
+    if (bf16) hipLaunchKernelGGL(k_amax_rht_rows<uint16_t>, dim3(g), dim3(kQuantThreads), 0, stream, (const uint16_t *)x, nch, sign_mask, amax_bits);
+    else hipLaunchKernelGGL(k_amax_rht_rows<float>, dim3(g), dim3(kQuantThreads), 0, stream, (const float *)x, nch, sign_mask, amax_bits);
+  } else {
+    const int64_t nu = (rows / 16) * cols;
+    unsigned g = grid_for(nu, kQuantThreads * 4, 4096);
+    if (bf16) hipLaunchKernelGGL(k_amax_rht_cols<uint16_t>, dim3(g), dim3(kQuantThreads), 0, stream, (const uint16_t *)x, rows, cols, sign_mask, amax_bits);
+    else hipLaunchKernelGGL(k_amax_rht_cols<float>, dim3(g), dim3(kQuantThreads), 0, stream, (const float *)x, rows, cols, sign_mask, amax_bits);
+  }
+  // pass 2: encode
+  const bool sr = (rounding == 1);
+  const int64_t nblocks = n / 16;
+  unsigned g = grid_for(nblocks);
+#define NVFP4_QROWS(T, S, R) hipLaunchKernelGGL((k_quant_rows<T, S, R>), dim3(g), dim3(kQuantThreads), 0, stream, (const T *)x, nblocks, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
+#define NVFP4_QCOLS(T, S, R) hipLaunchKernelGGL((k_quant_cols<T, S, R>), dim3(g), dim3(kQuantThreads), 0, stream, (const T *)x, rows, cols, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
+#define NVFP4_DISPATCH(MAC, T)                  \
+  do {                                          \
+    if (sr) { if (rht) MAC(T, true, true); else MAC(T, true, false); } \
+    else { if (rht) MAC(T, false, true); else MAC(T, false, false); } \
+  } while (0)
+  if (axis == 1) {
+    if (bf16) NVFP4_DISPATCH(NVFP4_QROWS, uint16_t);
+    else NVFP4_DISPATCH(NVFP4_QROWS, float);
+  } else {
+    if (bf16) NVFP4_DISPATCH(NVFP4_QCOLS, uint16_t);
+    else NVFP4_DISPATCH(NVFP4_QCOLS, float);
+  }
+#undef NVFP4_QROWS
+#undef NVFP4_QCOLS
+#undef NVFP4_DISPATCH
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *meta, int64_t outer,
+                             int64_t k, void *y, int y_dtype, hipStream_t stream) {
+  const int64_t nblocks = outer * (k / 16);
+  if (nblocks == 0) return hipSuccess;
+  unsigned g = grid_for(nblocks);
+  if (y_dtype == 0)
+    hipLaunchKernelGGL(k_dequant<float>, dim3(g), dim3(kQuantThreads), 0, stream, (const uint2 *)codes, scales, meta, nblocks, (float *)y);
+  else
+    hipLaunchKernelGGL(k_dequant<uint16_t>, dim3(g), dim3(kQuantThreads), 0, stream, (const uint2 *)codes, scales, meta, nblocks, (uint16_t *)y);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

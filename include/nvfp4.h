@@ -1,0 +1,163 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 linear-layer library.
+ *
+ * The library implements the 4-bit linear-layer path of NVIDIA's NVFP4
+ * pretraining recipe as described on these pages:
+ *   [P1] hyper.ai, "NVIDIA revolutioniert KI-Praetrainingsgeschwindigkeit mit
+ *        4-Bit-Genauigkeit" (body: 4-bit pretraining with dynamic scaling on
+ *        accelerated GEMMs).
+ *   [P3] aibuzzwire.news, Thinking Machines "End-to-End 4-Bit Training"
+ *        article; sections "Warum weniger Bits ein schnelleres Training
+ *        bedeuten" (rounding to the nearest representable value) and
+ *        "Unterschiedliche Phasen, unterschiedliche Regeln" (backward passes
+ *        are sensitive to rounding bias).
+ *   [P4] aisight.pl, "Koniec marnowania mocy. NVIDIA udowadnia, ze 4 bity
+ *        wystarcza do trenowania gigantow"; sections "Architektura NVFP4
+ *        kontra ograniczenia mikroskalowania" (16-element blocks, E4M3 block
+ *        scale, extra FP32 per-tensor scale) and "Technologie stabilizujace
+ *        proces treningowy" (random Hadamard transforms on weight gradients,
+ *        stochastic rounding).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named x, y, c and every pointer inside nvfp4_tensor are DEVICE
+ *    pointers owned by the caller; the library never allocates, frees or
+ *    retains them.  nvfp4_tensor structs themselves are HOST memory.
+ *  - hip_stream is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it; calls return without synchronising.
+ *  - Argument errors are reported synchronously, before anything is
+ *    launched.  NVFP4_ERR_HIP reports a failed launch.
+ *  - Sizes are int64_t and may be 0 (empty tensors are valid, see below).
+ *  - Element types: NVFP4_F32 (binary32) or NVFP4_BF16 (bfloat16).
+ *  - Thread safety: stateless; concurrent calls on different outputs are
+ *    fine.  The calls keep no scratch memory between launches.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = -1,   /* a required pointer is NULL                      */
+    NVFP4_ERR_SHAPE = -2,  /* negative size, K % 16 != 0, mismatched shapes   */
+    NVFP4_ERR_ENUM = -3,   /* unknown dtype / rounding / axis value           */
+    NVFP4_ERR_HIP = -4,    /* a HIP launch failed                             */
+    NVFP4_ERR_ALIGN = -5   /* a pointer or leading dimension is misaligned    */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+typedef enum { NVFP4_RNE = 0, NVFP4_SR = 1 } nvfp4_rounding;
+
+/*
+ * An NVFP4 tensor in its quantized layout [outer][k], k being the GEMM
+ * reduction length ([P4] "Architektura NVFP4 ..."):
+ *  codes  : u8 [outer][k/2]; element 2j of a row in the low nibble of byte j,
+ *           element 2j+1 in the high nibble.  A nibble is an E2M1 code:
+ *           bit 3 sign, bits 0-2 the magnitude 0, .5, 1, 1.5, 2, 3, 4, 6.
+ *           8-byte aligned.
+ *  scales : u8 [outer][k/16]; the OCP E4M3FN block scale of each 16-element
+ *           block along k (never NaN, at most 448).
+ *  meta   : f32 [2]; meta[0] = amax (the tensor maximum magnitude after the
+ *           optional transform), meta[1] = g = amax / 2688, the FP32 decode
+ *           scale.  4-byte aligned.
+ *  outer, k : k % 16 == 0.
+ * The value of element (o, kk) is e2m1(code) * e4m3(scale) * g.
+ */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    float *meta;
+    int64_t outer;
+    int64_t k;
+} nvfp4_tensor;
+
+/*
+ * nvfp4_quantize -- quantize a row-major [rows][cols] matrix x to NVFP4
+ * ([P4] "Architektura NVFP4 ..." for the format; [P3] "Warum weniger Bits
+ * ..." for nearest rounding; [P4] "Technologie stabilizujace ..." for
+ * stochastic rounding).
+ *
+ *  x        : device, x_dtype elements, row-major [rows][cols], 16-byte aligned.
+ *  axis     : 1 -> outer = rows, k = cols (blocks run along rows of x);
+ *             0 -> outer = cols, k = rows (blocks run down the columns of x;
+ *             the output is the transpose, as needed for the K-major operand
+ *             of a GEMM whose reduction runs over the rows of x).
+ *  rounding : NVFP4_RNE (nearest, ties to the even code, saturate at 6) or
+ *             NVFP4_SR (stochastic: round up iff r16 / 2^16 < fraction, with
+ *             r16 the 16 bits Philox4x32-10 assigns to the element).
+ *  seed, offset : Philox key = (lo32(seed), hi32(seed)); for the element with
+ *             output index i = o*k + kk the counter is (lo32(i/8), hi32(i/8),
+ *             lo32(offset), hi32(offset)) and r16 is half (i%2, low first) of
+ *             output word (i%8)/2.  Ignored for NVFP4_RNE.
+ *  out      : host struct; out->codes/scales/meta must point to buffers of
+ *             the sizes above and out->outer, out->k must equal the view's.
+ * Steps: amax over the whole tensor; s_enc = 2688/amax, per block
+ * S = E4M3_rne_sat(blockmax * (448/amax)); element code of x * (s_enc / S).
+ * amax == 0 gives all-zero scales and codes of +-0.  Non-finite input: meta[0]
+ * becomes Inf/NaN and the codes and scales are unspecified.  An empty tensor
+ * (outer == 0) writes meta = {0, 0} only.  Enqueues three kernels.
+ */
+int nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis,
+                   int rounding, uint64_t seed, uint64_t offset, nvfp4_tensor *out,
+                   void *hip_stream);
+
+/*
+ * nvfp4_rht_quantize -- as nvfp4_quantize, but each 16-element chunk along k
+ * is first replaced by (1/4) H16 diag(s) chunk, the 16-point random Hadamard
+ * transform ([P4] "Technologie stabilizujace ...": it spreads the outliers
+ * of the weight gradients).  H16 is the Sylvester Hadamard matrix
+ * H[i][j] = (-1)^popcount(i & j) and s_j = -1 where bit j of sign_mask is
+ * set.  The butterfly runs in binary32 with stages 1, 2, 4, 8 (lower index
+ * a+b, upper a-b).  amax and block maxima are those of the transformed
+ * values.  Both operands of a weight-gradient GEMM must use the same
+ * sign_mask along their shared reduction dimension; the transform then
+ * cancels in the product.
+ */
+int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis,
+                       int rounding, uint64_t seed, uint64_t offset, uint16_t sign_mask,
+                       nvfp4_tensor *out, void *hip_stream);
+
+/*
+ * nvfp4_dequantize -- y[o][kk] = (e2m1(code) * e4m3(scale)) * g in binary32
+ * (the first product is exact, the second rounds once); bf16 output is the
+ * nearest-even rounding of that value.  y: device [q->outer][q->k] row-major
+ * in the QUANTIZED layout (an axis-0 tensor comes back transposed), 16-byte
+ * aligned.  Defines the values the GEMM multiplies ([P3] "Warum weniger Bits
+ * ..." measures quantization error against these decoded values).
+ */
+int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stream);
+
+/*
+ * nvfp4_gemm -- the block-scaled NVFP4 GEMM with FP32 accumulation
+ * ([P1] body: accelerated 4-bit GEMMs; [P4] "Architektura NVFP4 ...").
+ *
+ *   C[m][n] = g_A * g_B * sum_k (qA*SA)[m][k] * (qB*SB)[n][k]
+ *
+ *  a : M x K NVFP4 tensor (a->outer = M), b : N x K (b->outer = N), a->k ==
+ *      b->k.  Both operands are K-contiguous ("TN"): fprop Y = X W^T takes
+ *      a = X (axis 1), b = W (axis 1); dgrad dX = dY W takes a = dY (axis 1),
+ *      b = W quantized on axis 0; wgrad dW = X^T dY takes a = X (axis 0) and
+ *      b = dY (axis 0).
+ *  c : device, row-major [M][ldc], c_dtype NVFP4_F32 or NVFP4_BF16 (nearest
+ *      even of the f32 result), ldc >= N, 4-byte aligned (f32) / 2-byte (bf16).
+ * Accuracy: every element within 1e-5 * g_A g_B sum_k |(qA SA)(qB SB)| of the
+ * exact value (each 16-element partial product sum is exact in f32; the
+ * accumulation rounds once per 16-block step).  Deterministic: one kernel,
+ * no atomics, fixed summation order.  M == 0 or N == 0: nothing is written;
+ * K == 0: C is set to zero.
+ */
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
+               int64_t ldc, void *hip_stream);
+
+/* Human-readable name of a status code (static string). */
+const char *nvfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every symbol include/nvfp4.h declares, and
+reports argument errors synchronously, before anything is launched (so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_amax_reduce_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        pytest.fail("libnvfp4.so not built (run __graft_entry__.build())")
+    return nv.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(nv.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.nvfp4_status_string(code)
+    assert L.nvfp4_status_string(12345) == b"unknown status"
+
+
+FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced
+
+# Every call below passes at least one invalid argument, so validation must
+# return before any launch.  The fake device addresses would fault a real
+# GPU if a validation bug let a launch through, so these tests only run
+# where no GPU is visible.
+_no_gpu = pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                             reason="fake-pointer argument tests run only without a GPU")
+
+
+def _t(outer, k, codes=FAKE, scales=FAKE, meta=FAKE):
+    return nv._CTensor(codes, scales, meta, outer, k)
+
+
+@_no_gpu
+def test_quantize_argument_errors(L):
+    q = _t(16, 32)
+    by = ctypes.byref
+    assert L.nvfp4_quantize(FAKE, 1, 16, 32, 1, 0, 0, 0, None, None) == -1      # out NULL
+    assert L.nvfp4_quantize(FAKE, 2, 16, 32, 1, 0, 0, 0, by(q), None) == -3     # dtype
+    assert L.nvfp4_quantize(FAKE, 1, 16, 32, 1, 7, 0, 0, by(q), None) == -3     # rounding
+    assert L.nvfp4_quantize(FAKE, 1, 16, 32, 2, 0, 0, 0, by(q), None) == -3     # axis
+    assert L.nvfp4_quantize(FAKE, 1, -1, 32, 1, 0, 0, 0, by(q), None) == -2     # negative
+    q24 = _t(16, 24)
+    assert L.nvfp4_quantize(FAKE, 1, 16, 24, 1, 0, 0, 0, by(q24), None) == -2   # K % 16
+    assert L.nvfp4_quantize(FAKE, 1, 16, 48, 1, 0, 0, 0, by(q), None) == -2     # out shape
+    assert L.nvfp4_quantize(FAKE, 1, 16, 32, 0, 0, 0, 0, by(q), None) == -2     # axis-0 view is 32x16
+    assert L.nvfp4_quantize(None, 1, 16, 32, 1, 0, 0, 0, by(q), None) == -1     # x NULL
+    assert L.nvfp4_quantize(FAKE + 2, 1, 16, 32, 1, 0, 0, 0, by(q), None) == -5 # x misaligned
+    qn = _t(16, 32, meta=0)
+    assert L.nvfp4_quantize(FAKE, 1, 16, 32, 1, 0, 0, 0, by(qn), None) == -1    # meta NULL
+    qa = _t(16, 32, codes=FAKE + 4)
+    assert L.nvfp4_quantize(FAKE, 1, 16, 32, 1, 0, 0, 0, by(qa), None) == -5    # codes misaligned
+    assert L.nvfp4_rht_quantize(FAKE, 1, 16, 24, 1, 0, 0, 0, 0xFFFF, by(q24), None) == -2
+
+
+@_no_gpu
+def test_dequantize_argument_errors(L):
+    by = ctypes.byref
+    assert L.nvfp4_dequantize(None, FAKE, 0, None) == -1
+    assert L.nvfp4_dequantize(by(_t(16, 24)), FAKE, 0, None) == -2
+    assert L.nvfp4_dequantize(by(_t(16, 32)), FAKE, 5, None) == -3
+    assert L.nvfp4_dequantize(by(_t(16, 32)), None, 0, None) == -1
+    assert L.nvfp4_dequantize(by(_t(16, 32)), FAKE + 8, 0, None) == -5
+
+
+@_no_gpu
+def test_gemm_argument_errors(L):
+    by = ctypes.byref
+    a, b = _t(8, 32), _t(4, 32)
+    assert L.nvfp4_gemm(None, by(b), FAKE, 0, 4, None) == -1
+    assert L.nvfp4_gemm(by(a), by(_t(4, 48)), FAKE, 0, 4, None) == -2     # K mismatch
+    assert L.nvfp4_gemm(by(a), by(b), FAKE, 3, 4, None) == -3             # dtype
+    assert L.nvfp4_gemm(by(a), by(b), FAKE, 0, 3, None) == -2             # ldc < N
+    assert L.nvfp4_gemm(by(a), by(b), None, 0, 4, None) == -1             # C NULL
+    assert L.nvfp4_gemm(by(a), by(b), FAKE + 2, 0, 4, None) == -5         # C misaligned (f32)
+    assert L.nvfp4_gemm(by(_t(-1, 32)), by(b), FAKE, 0, 4, None) == -2
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(nv.NVFP4Error, match="GPU"):
+        nv.nvfp4_quantize(torch.zeros(16, 32))
