@@ -8,190 +8,289 @@
 //
 //   C[m][n] = gA * gB * sum_k (qA * SA)[m][k] * (qB * SB)[n][k]
 //
-// Design for CDNA4: gfx950's block-scaled MFMA forms take power-of-two
-// (E8M0) scales per 32 elements, which cannot represent an E4M3 scale per 16
-// elements.  Each element is therefore decoded exactly in registers: the
-// hardware FP4->F16 conversion gives q, and one packed f16 multiply by the
-// block scale S gives q*S, which has at most 6 significant bits and lies in
-// [2^-10, 2688], so it is exact in f16.  The exact products feed
-// v_mfma_f32_32x32x16_f16 with f32 accumulators; every 16-block partial sum
-// is exact, so the accumulation rounds once per 16-element step.
+// Design for CDNA4.  gfx950's block-scaled MFMA forms take one power-of-two
+// (E8M0) scale per 32 elements, which cannot represent an E4M3 scale per 16
+// elements, so every element is decoded exactly: the hardware FP4->F16
+// conversion gives q and one packed f16 multiply by the block scale gives
+// q*S.  q*S has at most 6 significant bits and lies in [2^-10, 2688], so it
+// is exact in f16, and every 16-element partial sum of the f16 MFMA is exact
+// in f32.
 //
-// Tiling: a 256-thread workgroup computes a 128x128 tile of C; each of its
-// four waves owns a 64x64 sub-tile (2x2 MFMA tiles of 32x32).  The K loop
-// stages 128 K-elements of packed codes (64 bytes per row) and their eight
-// scales per row in LDS; each lane then reads 16 bytes (32 codes) of one row
-// per 64-K half.  Lane l of an MFMA fragment holds K positions
-// 64*kk + 32*(l/32) + 8*s + [0,8) for step s: a permutation of K applied
-// identically to A and B, which leaves the sum unchanged.
+// Decode once per workgroup.  A 256-thread workgroup computes a 256x256 tile
+// of C with four waves of 128x128 (4x4 v_mfma_f32_32x32x16_f16 tiles, 256
+// f32 accumulators per lane).  K advances 64 elements per stage.  Each stage
+// the workgroup loads the packed codes (32 bytes per row) and block scales of
+// its 256 A rows and 256 B rows with range-checked buffer loads, decodes them
+// ONCE to f16 and writes them to LDS in MFMA operand order: a 32x16 operand
+// fragment is 1 KB, lane l's 16 bytes at offset 16*l, so both the decoding
+// writes and the MFMA operand reads are contiguous 1 KB wave accesses with
+// no bank conflicts.  Two stages are double-buffered (2 x 64 KB of LDS); the
+// decode of stage s+1 and the global loads of stage s+2 are issued between
+// the MFMAs of stage s.  Decoding per workgroup instead of per wave halves
+// the conversion work (each operand row feeds two waves).
+//
+// K order inside a fragment: lane l (row l%32, half h = l/32) holds the 8
+// consecutive K positions 16*ks + 8*h .. +7 of K step ks, for A and B alike,
+// which is the operand layout the MFMA sums over.
+//
+// Grid: one workgroup per 256x256 tile.  Workgroups are dealt round-robin to
+// the eight XCDs (pid % 8); the tile index is remapped so each XCD works on
+// a contiguous range of tiles, ordered in groups of 8 tile rows, so that the
+// tiles resident on one XCD share A rows and B columns in its L2.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
+
+#include <type_traits>
 
 namespace nvfp4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int BKB = BK / 2;        // code bytes per row per K tile
-constexpr int BKS = BK / 16;       // scales per row per K tile
-constexpr int LDSB = BKB + 16;     // padded LDS row stride of the code tiles
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
+constexpr int kFrag = 1024;                             // one 32x16 f16 operand fragment
+constexpr int kKSteps = BK / 16;                        // 4 MFMA K steps per stage
+constexpr int kHalfStage = (BM / 32) * kKSteps * kFrag; // 32 KB: A (or B) part of a stage
+constexpr int kStage = 2 * kHalfStage;                  // 64 KB
+constexpr int kGroupM = 8;                              // tile rows per L2 group
+constexpr int kXcds = 8;
 
-// 16 code bytes of row `row` starting at byte `kb` (K/2 bytes per row);
-// zero outside the matrix.  The tail of a row may hold only 8 valid bytes.
-__device__ __forceinline__ uint4 load_codes16(const uint8_t *p, int64_t rows, int64_t KB, int64_t row,
-                                              int64_t kb, bool al16) {
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (row >= rows) return v;
-  const uint8_t *src = p + row * KB + kb;
-  if (kb + 16 <= KB) {
-    if (al16) {
-      v = *reinterpret_cast<const uint4 *>(src);
-    } else {
-      uint2 a = *reinterpret_cast<const uint2 *>(src);
-      uint2 b = *reinterpret_cast<const uint2 *>(src + 8);
-      v = make_uint4(a.x, a.y, b.x, b.y);
-    }
-  } else if (kb + 8 <= KB) {
-    uint2 a = *reinterpret_cast<const uint2 *>(src);
-    v = make_uint4(a.x, a.y, 0, 0);
-  }
-  return v;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Range-checked buffer view of one operand's tile rows: loads past
+// `num_bytes` return zero, which pads the M and N edges.
+struct TileView {
+  __amdgpu_buffer_rsrc_t codes;
+  __amdgpu_buffer_rsrc_t scales;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  // 0x00020000: 32-bit data format word of a raw (stride 0) buffer on gfx9.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// 4 scale bytes of row `row` starting at scale index `ks`; zero outside.
-__device__ __forceinline__ uint32_t load_scales4(const uint8_t *p, int64_t rows, int64_t KS, int64_t row,
-                                                 int64_t ks) {
-  uint32_t v = 0;
-  if (row >= rows) return v;
-  const uint8_t *src = p + row * KS;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    if (ks + t < KS) v |= (uint32_t)src[ks + t] << (8 * t);
-  return v;
-}
+// Global-memory image of one thread's share of a stage: four 16-byte code
+// chunks (two A rows, two B rows; 32 K positions each) and their two block
+// scales apiece.
+struct StageRegs {
+  u32x4 c[4];
+  uint32_t s[4];
+};
 
-// 8 E2M1 codes (one 32-bit word, element 0 in the low nibble) -> 8 exact
-// f16 values of q * S.
-__device__ __forceinline__ half8_t decode8(uint32_t w, _Float16 S) {
-  half2_t s2 = {S, S};
-  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
-  half8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  return r;
+// 8 codes (one word, element 0 in the low nibble) times the f16 pair of
+// block scales selected by `hi` -> 8 exact f16 values, as 4 words.
+__device__ __forceinline__ u32x4 decode8(uint32_t w, half2_t s2, bool hi) {
+  const half2_t s = hi ? (half2_t){s2[1], s2[1]} : (half2_t){s2[0], s2[0]};
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return (u32x4){__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
 }
-
-__device__ __forceinline__ _Float16 scale_f16(uint32_t b) { return (_Float16)e4m3_to_f32(b); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <bool OUT_BF16>
-__global__ void __launch_bounds__(kThreads) k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
-                                                       const float *__restrict__ metaA, const uint8_t *__restrict__ B,
-                                                       const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
-                                                       int64_t M, int64_t N, int64_t K, void *__restrict__ C,
-                                                       int64_t ldc) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * LDSB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[BN * LDSB];
-  __shared__ __attribute__((aligned(16))) uint8_t sSA[BM * BKS];
-  __shared__ __attribute__((aligned(16))) uint8_t sSB[BN * BKS];
+template <bool OUT_BF16, bool SCALE16>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
+             const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
+             int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int64_t KB = K / 2, KS = K / 16;
-  const bool alA = (KB % 16 == 0) && (((uintptr_t)A & 15) == 0);
-  const bool alB = (KB % 16 == 0) && (((uintptr_t)B & 15) == 0);
 
-  float16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  const int ntiles = tiles_m * tiles_n;
+  const int pid = blockIdx.x;
+  const int xcd = pid % kXcds, local = pid / kXcds;
+  const int q = ntiles / kXcds, r = ntiles % kXcds;
+  const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int per_group = kGroupM * tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int tm = first_m + (logical % per_group) % gsz;
+  const int tn = (logical % per_group) / gsz;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  for (int64_t k0 = 0; k0 < K; k0 += BK) {
-    uint4 ra[2], rb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads * i, r = c >> 2, q = c & 3;
-      ra[i] = load_codes16(A, M, KB, m0 + r, k0 / 2 + 16 * q, alA);
-      rb[i] = load_codes16(B, N, KB, n0 + r, k0 / 2 + 16 * q, alB);
-    }
-    const int sr = tid >> 1, s4 = (tid & 1) * 4;
-    const uint32_t rsa = load_scales4(SA, M, KS, m0 + sr, k0 / 16 + s4);
-    const uint32_t rsb = load_scales4(SB, N, KS, n0 + sr, k0 / 16 + s4);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads * i, r = c >> 2, q = c & 3;
-      *reinterpret_cast<uint4 *>(&sA[r * LDSB + 16 * q]) = ra[i];
-      *reinterpret_cast<uint4 *>(&sB[r * LDSB + 16 * q]) = rb[i];
-    }
-    *reinterpret_cast<uint32_t *>(&sSA[sr * BKS + s4]) = rsa;
-    *reinterpret_cast<uint32_t *>(&sSB[sr * BKS + s4]) = rsb;
-    __syncthreads();
+  // ---- operand views restricted to this tile's rows
+  const uint32_t row_bytes = (uint32_t)(K / 2), row_scales = (uint32_t)(K / 16);
+  const uint32_t rows_a = (uint32_t)(M - m0 < BM ? M - m0 : BM);
+  const uint32_t rows_b = (uint32_t)(N - n0 < BN ? N - n0 : BN);
+  TileView va{make_rsrc(A + m0 * row_bytes, rows_a * row_bytes), make_rsrc(SA + m0 * row_scales, rows_a * row_scales)};
+  TileView vb{make_rsrc(B + n0 * row_bytes, rows_b * row_bytes), make_rsrc(SB + n0 * row_scales, rows_b * row_scales)};
 
+  // ---- this thread's decode share: chunk j covers tile row R_j (A for
+  // j < 2, B for j >= 2), K half c = lane / 32 of the 64-wide stage.
+  const int c = lh;
+  uint32_t code_off[4], scale_off[4], lds_off[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      half8_t af[2][4], bf[2][4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + 32 * i + l32;
-        const uint4 w = *reinterpret_cast<const uint4 *>(&sA[row * LDSB + kk * 32 + 16 * lh]);
-        const _Float16 s0 = scale_f16(sSA[row * BKS + kk * 4 + 2 * lh]);
-        const _Float16 s1 = scale_f16(sSA[row * BKS + kk * 4 + 2 * lh + 1]);
-        af[i][0] = decode8(w.x, s0);
-        af[i][1] = decode8(w.y, s0);
-        af[i][2] = decode8(w.z, s1);
-        af[i][3] = decode8(w.w, s1);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = wn * 64 + 32 * j + l32;
-        const uint4 w = *reinterpret_cast<const uint4 *>(&sB[col * LDSB + kk * 32 + 16 * lh]);
-        const _Float16 s0 = scale_f16(sSB[col * BKS + kk * 4 + 2 * lh]);
-        const _Float16 s1 = scale_f16(sSB[col * BKS + kk * 4 + 2 * lh + 1]);
-        bf[j][0] = decode8(w.x, s0);
-        bf[j][1] = decode8(w.y, s0);
-        bf[j][2] = decode8(w.z, s1);
-        bf[j][3] = decode8(w.w, s1);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i][s], bf[j][s], acc[i][j], 0, 0, 0);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int g = 4 * j + wave;             // 32-row group of the 512 stage rows
+    const int rg = g & 7;                   // row group within the operand
+    const uint32_t row = 32 * rg + l32;     // row within the operand tile
+    code_off[j] = row * row_bytes + 16 * c;
+    scale_off[j] = row * row_scales + 2 * c;
+    // fragment (rg, ks = 2c + wd/2), lane slot l32 + 32*(wd%2); wd added later
+    lds_off[j] = (g >> 3) * kHalfStage + (rg * kKSteps + 2 * c) * kFrag + l32 * 16;
   }
 
-  // epilogue: C = (acc * gA) * gB; lane holds column l32 and rows
-  // 8*a + 4*lh + b of each 32x32 tile (register 4*a + b).
+  // Global loads of one chunk of a stage into registers.  TAIL masks the K
+  // positions past K (the last, partial stage and any stage beyond it come
+  // out zero).
+  auto load_chunk = [&](StageRegs &st, int j, int64_t k0, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const uint32_t kb = (uint32_t)(k0 / 2), ksc = (uint32_t)(k0 / 16);
+    const TileView &v = (j < 2) ? va : vb;
+    st.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v.codes, code_off[j] + kb, 0, 0));
+    if constexpr (SCALE16) {
+      st.s[j] = __builtin_amdgcn_raw_buffer_load_b16(v.scales, scale_off[j] + ksc, 0, 0);
+    } else {  // a row's scales may start at an odd address
+      st.s[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(v.scales, scale_off[j] + ksc, 0, 0) |
+                ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(v.scales, scale_off[j] + ksc + 1, 0, 0) << 8);
+    }
+    if constexpr (TAIL) {
+      const int64_t kvalid = K - k0 - 32 * c;   // valid K positions of this thread's chunk
+      const uint32_t keep_lo = kvalid >= 16 ? ~0u : 0u, keep_hi = kvalid >= 32 ? ~0u : 0u;
+      st.c[j].x &= keep_lo;
+      st.c[j].y &= keep_lo;
+      st.c[j].z &= keep_hi;
+      st.c[j].w &= keep_hi;
+      st.s[j] &= (keep_lo & 0xFFu) | (keep_hi & 0xFF00u);
+    }
+  };
+  auto load_stage = [&](StageRegs &st, int64_t k0, auto tail) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_chunk(st, j, k0, tail);
+  };
+
+  // Decode word wd (8 codes) of chunk j into the LDS stage buffer: word wd
+  // goes to K step 2c + wd/2, lane slot l32 + 32*(wd%2).
+  auto decode_word = [&](const StageRegs &st, int j, int wd, uint8_t *buf) {
+    const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.s[j], 1.0f, false);
+    const uint32_t w = wd == 0 ? st.c[j].x : wd == 1 ? st.c[j].y : wd == 2 ? st.c[j].z : st.c[j].w;
+    uint8_t *dst = buf + lds_off[j] + (wd >> 1) * kFrag + (wd & 1) * (32 * 16);
+    *reinterpret_cast<u32x4 *>(dst) = decode8(w, s2, wd >= 2);
+  };
+  auto store_stage = [&](const StageRegs &st, uint8_t *buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) decode_word(st, j, wd, buf);
+  };
+
+  float16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int a_frag0 = (4 * wm) * kKSteps * kFrag + lane * 16;
+  const int b_frag0 = kHalfStage + (4 * wn) * kKSteps * kFrag + lane * 16;
+
+  // The 8 operand fragments (4 A row tiles, 4 B column tiles) of K step ks.
+  auto read_frags = [&](const uint8_t *cur, int ks, half8_t *af, half8_t *bf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const half8_t *>(cur + a_frag0 + (i * kKSteps + ks) * kFrag);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bf[j] = *reinterpret_cast<const half8_t *>(cur + b_frag0 + (j * kKSteps + ks) * kFrag);
+  };
+
+  using Full = std::false_type;
+  using Tail = std::true_type;
+  const int nk = (int)((K + BK - 1) / BK);   // stages
+  const int nfull = (int)(K / BK);           // stages with all 64 K positions valid
+  StageRegs st;
+  load_stage(st, 0, Tail{});
+  store_stage(st, smem);
+  load_stage(st, BK, Tail{});
+  __syncthreads();
+
+  // Main loop: stage s is multiplied from LDS while stage s+1 is decoded
+  // from registers into the other buffer and stage s+2 is loaded.  The
+  // instruction order is fixed by hand (sched_barrier fences): each group of
+  // four MFMAs (128 cycles of the matrix core) is followed by one decode unit
+  // (one word: 4 conversions, 4 packed multiplies, one 16-byte LDS write), so
+  // the VALU work of the decode runs while the MFMAs execute; the operand
+  // fragments of the next K step are read one step ahead; a chunk's global
+  // loads for stage s+2 are issued as soon as its registers are decoded.
+  half8_t af[2][4], bf[2][4];
+  int s = 0;
+  for (; s + 2 < nfull; ++s) {
+    const uint8_t *cur = smem + (s & 1) * kStage;
+    uint8_t *nxt = smem + ((s & 1) ^ 1) * kStage;
+    const int64_t k2 = (int64_t)(s + 2) * BK;
+    read_frags(cur, 0, af[0], bf[0]);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + 1 < kKSteps) read_frags(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = 4 * ks + i;       // decode unit: chunk u/4, word u%4
+        decode_word(st, u >> 2, u & 3, nxt);
+        if ((u & 3) == 3) load_chunk(st, u >> 2, k2, Full{});
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+  // Tail: the last stages (stage s+2 may be partial or past K: zeros).
+  for (; s < nk; ++s) {
+    const uint8_t *cur = smem + (s & 1) * kStage;
+    uint8_t *nxt = smem + ((s & 1) ^ 1) * kStage;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      read_frags(cur, ks, af[0], bf[0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
+    }
+    store_stage(st, nxt);
+    load_stage(st, (int64_t)(s + 2) * BK, Tail{});
+    __syncthreads();
+  }
+
+  // ---- epilogue: C = (acc * gA) * gB.  Lane holds column l32 and rows
+  // 8*(e/4) + 4*lh + e%4 of each 32x32 tile; row offsets are uniform, so
+  // the per-store address is one lane base plus a scalar offset.
   const float gA = metaA[1], gB = metaB[1];
+  const int64_t row_l = m0 + wm * 128 + 4 * lh, col_l = n0 + wn * 128 + l32;
+  const bool full_tile = (m0 + BM <= M) && (n0 + BN <= N);
+  using OutT = typename std::conditional<OUT_BF16, uint16_t, float>::type;
+  OutT *base = reinterpret_cast<OutT *>(C) + row_l * ldc + col_l;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + 32 * j + l32;
-      if (col >= N) continue;
+    for (int e = 0; e < 16; ++e) {
+      const int roff = 32 * i + 8 * (e >> 2) + (e & 3);
+      if (!full_tile && row_l + roff >= M) continue;
+      OutT *prow = base + (int64_t)roff * ldc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row >= M) continue;
-        const float v = (acc[i][j][r] * gA) * gB;
-        if (OUT_BF16)
-          reinterpret_cast<uint16_t *>(C)[row * ldc + col] = f32_to_bf16_rne(v);
+      for (int j = 0; j < 4; ++j) {
+        if (!full_tile && col_l + 32 * j >= N) continue;
+        const float v = (acc[i][j][e] * gA) * gB;
+        if constexpr (OUT_BF16)
+          prow[32 * j] = f32_to_bf16_rne(v);
         else
-          reinterpret_cast<float *>(C)[row * ldc + col] = v;
+          prow[32 * j] = v;
       }
     }
   }
@@ -218,13 +317,22 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
     hipLaunchKernelGGL(k_zero_c, dim3(g), dim3(256), 0, stream, c, M, N, ldc, c_dtype == 0 ? 4 : 2);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  if (c_dtype == 0)
-    hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, b_codes,
-                       b_scales, b_meta, M, N, K, c, ldc);
-  else
-    hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, b_codes,
-                       b_scales, b_meta, M, N, K, c, ldc);
+  // The buffer views address one 256-row tile with 32-bit offsets.
+  if ((int64_t)BM * (K / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)tiles);
+  // 16-bit scale loads need an even number of scales per row (K % 32 == 0).
+  const bool s16 = (K % 32) == 0;
+#define NVFP4_GEMM_LAUNCH(OB, S16)                                                                          \
+  hipLaunchKernelGGL((k_gemm_nvfp4<OB, S16>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, \
+                     b_codes, b_scales, b_meta, M, N, K, c, ldc)
+  if (c_dtype == 0) {
+    if (s16) NVFP4_GEMM_LAUNCH(false, true); else NVFP4_GEMM_LAUNCH(false, false);
+  } else {
+    if (s16) NVFP4_GEMM_LAUNCH(true, true); else NVFP4_GEMM_LAUNCH(true, false);
+  }
+#undef NVFP4_GEMM_LAUNCH
   return hipGetLastError();
 }
 
