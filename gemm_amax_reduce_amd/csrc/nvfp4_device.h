@@ -3,7 +3,7 @@
 // Format ([P4] aisight.pl "Koniec marnowania mocy ...", section "Architektura
 // NVFP4 kontra ograniczenia mikroskalowania"): 4-bit E2M1 elements, one
 // E4M3 scale per 16 elements along the reduction dimension, one FP32 scale
-// per tensor.  Every helper here is written for CDNA4 and relies on three
+// per tensor.  Every helper here is written for CDNA4 and relies on four
 // measured properties of gfx950:
 //  * v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds binary32 to E2M1
 //    nearest-even (ties to the even code), saturates at 6 and keeps the sign
@@ -11,6 +11,9 @@
 //  * v_cvt_scalef32_pk_f16_fp4 with scale 1.0 decodes E2M1 exactly (its scale
 //    operand only contributes its exponent, so the E4M3 block scale is
 //    applied with a separate exact f16 multiply);
+//  * v_cvt_scalef32_sr_pk_fp4_f32 with scale 1.0 rounds the first value of
+//    its pair up iff rand >= (1 - frac) * 2^32 (add-and-truncate on the
+//    discarded fraction), saturating at 6 and keeping the sign;
 //  * v_cvt_f32_fp8 decodes OCP E4M3FN, binary32 denormals are kept and
 //    __fdiv_rn is the correctly rounded quotient.
 #pragma once
@@ -97,57 +100,73 @@ __device__ __forceinline__ uint32_t encode8_rne(const float *v) {
   return w;
 }
 
-// Stochastic rounding of one value with 16 random bits r16: with lo the
-// largest grid magnitude <= |v| and frac the position between lo and the
-// next grid point, round up iff r16 < frac * 2^16 ([P4] "Technologie
-// stabilizujace ...": stochastic rounding removes the systematic error).
-// The binade of |v| picks the grid spacing (0.5 below 2, 1 in [2,4), 2 in
-// [4,6)); scaling by its inverse (an exact power of two) turns the grid into
-// the integers, so floor and the remainder are exact.
-__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t r16) {
-  uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-  float a = __builtin_fabsf(v);
-  uint32_t e = __float_as_uint(a) >> 23;
-  uint32_t c = min(max(e, 127u), 129u);           // 127: a<2, 128: [2,4), 129: >=4
-  float inv_step = __uint_as_float((255u - c) << 23);  // 2, 1, 0.5
-  float t = a * inv_step;
-  float f = __builtin_floorf(t);
-  float frac = t - f;
-  uint32_t up = ((float)r16 < frac * 65536.0f) ? 1u : 0u;
-  uint32_t code = (uint32_t)f + up + 2u * (c - 127u);
-  code = (a < 6.0f) ? code : 7u;                  // saturation (and NaN -> 7)
-  return sign | code;
+// Stochastic rounding ([P4] "Technologie stabilizujace ...": stochastic
+// rounding removes the systematic error of ordinary rounding).  Rule: with
+// frac the position of |v| between its two neighbouring grid values, round
+// up iff frac + (r16 + 1/2) / 2^16 >= 1 -- add a uniform offset of
+// (r16 + 1/2) / 2^16 grid steps, then truncate.  gfx950's
+// v_cvt_scalef32_sr_pk_fp4_f32 (scale 1) computes, for the FIRST value of
+// its pair, exactly "round up iff rand >= (1 - frac) * 2^32" (checked against
+// the exact rational rule on 3.8 M (value, rand) pairs covering every
+// binade, the saturation at 6, signs and tiny values), so rand =
+// (r16 << 16) | 0x8000 gives the rule above.  The second value of a pair
+// sees rand << 1, which would tie neighbouring elements' random bits, so
+// each conversion carries one element with +0 as its partner: byte 0 of the
+// result is then the element's code (the partner's code 0 in the high
+// nibble).  Only byte 0 is used -- the compiler does not keep the other
+// bytes of the destination -- and v_perm_b32 gathers the codes.
+__device__ __forceinline__ uint32_t sr_code_byte(float v, uint32_t rand) {
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (float2_t){v, 0.0f}, rand, 1.0f, 0);
+}
+
+// Byte 0 of a, b, c, d -> bytes 0..3 of the result.
+__device__ __forceinline__ uint32_t gather_byte0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);   // [a0, b0, 0, 0]
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000C0Cu);   // [0, 0, c0, d0]
+  return ab | cd;
+}
+
+// Four Philox words w[0..3] carry the 16-bit draws of elements 0..7
+// (element 2j: low half of w[j], element 2j+1: high half).  Returns the
+// eight stochastically rounded codes of v[0..7], element 0 lowest.
+__device__ __forceinline__ uint32_t encode8_sr(const float *v, const uint32_t *w) {
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[2 * j] = sr_code_byte(v[2 * j], (w[j] << 16) | 0x8000u);
+    c[2 * j + 1] = sr_code_byte(v[2 * j + 1], (w[j] & 0xFFFF0000u) | 0x8000u);
+  }
+  const uint32_t ev = gather_byte0(c[0], c[2], c[4], c[6]);
+  const uint32_t od = gather_byte0(c[1], c[3], c[5], c[7]);
+  return ev | (od << 4);
 }
 
 // -------------------------------------------------------------- Philox ----
 // Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64 products
 // with the multipliers 0xD2511F53 / 0xCD9E8D57, word permutation, and a key
-// schedule bumped by the Weyl constants 0x9E3779B9 / 0xBB67AE85.
+// schedule bumped by the Weyl constants 0x9E3779B9 / 0xBB67AE85.  Each
+// product is one 64-bit multiply (v_mad_u64_u32 gives both halves; measured
+// cheaper on gfx950 than a v_mul_hi_u32 / v_mul_lo_u32 pair) and each
+// three-way XOR one v_bitop3_b32 (truth table 0x96).  The key words are wave-uniform (scalar).
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
-    uint32_t lo0 = 0xD2511F53u * c.x;
-    uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
-    uint32_t lo1 = 0xCD9E8D57u * c.z;
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96), (uint32_t)p1,
+                   __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96), (uint32_t)p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
   return c;
 }
 
-// 16-bit random values for the 8 elements with output indices 8g .. 8g+7:
-// counter (lo(g), hi(g), lo(offset), hi(offset)), key (lo(seed), hi(seed));
-// element 8g+j takes half (j & 1) (low first) of word j >> 1.
-__device__ __forceinline__ void sr_bits8(uint64_t g, uint64_t seed, uint64_t offset, uint32_t *r) {
-  uint4 w = philox4x32_10(make_uint4((uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset,
-                                     (uint32_t)(offset >> 32)),
-                          (uint32_t)seed, (uint32_t)(seed >> 32));
-  r[0] = w.x & 0xFFFFu; r[1] = w.x >> 16;
-  r[2] = w.y & 0xFFFFu; r[3] = w.y >> 16;
-  r[4] = w.z & 0xFFFFu; r[5] = w.z >> 16;
-  r[6] = w.w & 0xFFFFu; r[7] = w.w >> 16;
+// Philox output for the 8 elements with output indices 8g .. 8g+7: counter
+// (lo(g), hi(g), lo(offset), hi(offset)), key (lo(seed), hi(seed)); element
+// 8g+j takes half (j & 1) (low first) of word j >> 1.
+__device__ __forceinline__ uint4 sr_words8(uint64_t g, uint64_t seed, uint64_t offset) {
+  return philox4x32_10(make_uint4((uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)),
+                       (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
 // ----------------------------------------------------------------- RHT ----
@@ -219,15 +238,9 @@ __device__ __forceinline__ uint2 encode16(const float *y, float m, uint64_t blk,
   if (!SR) {
     return make_uint2(encode8_rne(v), encode8_rne(v + 8));
   } else {
-    uint32_t r[16];
-    sr_bits8(2 * blk, seed, offset, r);
-    sr_bits8(2 * blk + 1, seed, offset, r + 8);
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      w0 |= e2m1_sr(v[j], r[j]) << (4 * j);
-      w1 |= e2m1_sr(v[8 + j], r[8 + j]) << (4 * j);
-    }
+    const uint4 a = sr_words8(2 * blk, seed, offset), b = sr_words8(2 * blk + 1, seed, offset);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    const uint32_t w0 = encode8_sr(v, wa), w1 = encode8_sr(v + 8, wb);
     return make_uint2(w0, w1);
   }
 }

@@ -87,8 +87,10 @@ typedef struct {
  *             the output is the transpose, as needed for the K-major operand
  *             of a GEMM whose reduction runs over the rows of x).
  *  rounding : NVFP4_RNE (nearest, ties to the even code, saturate at 6) or
- *             NVFP4_SR (stochastic: round up iff r16 / 2^16 < fraction, with
- *             r16 the 16 bits Philox4x32-10 assigns to the element).
+ *             NVFP4_SR (stochastic: with frac the position of |v| between
+ *             its two neighbouring grid values, round up iff
+ *             frac + (r16 + 1/2) / 2^16 >= 1, r16 being the 16 bits
+ *             Philox4x32-10 assigns to the element; saturate at 6).
  *  seed, offset : Philox key = (lo32(seed), hi32(seed)); for the element with
  *             output index i = o*k + kk the counter is (lo32(i/8), hi32(i/8),
  *             lo32(offset), hi32(offset)) and r16 is half (i%2, low first) of

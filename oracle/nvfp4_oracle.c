@@ -104,10 +104,14 @@ uint8_t oracle_e2m1_rne(float v)
 /* Stochastic rounding onto the E2M1 grid ([P4] "Technologie stabilizujace
  * ...": stochastic rounding removes the systematic error of ordinary
  * rounding; [P3] "Unterschiedliche Phasen ...": the backward pass tolerates
- * noise but not bias).  Reading: with lo the largest grid magnitude <= |v|
- * and hi the next one, round up with probability frac = (|v|-lo)/(hi-lo),
- * decided by 16 random bits r16: up iff r16 / 2^16 < frac.  |v| >= 6
- * saturates to 6.  A value on the grid has frac = 0 and never moves. */
+ * noise but not bias).  Reading: the textbook definition -- add a uniform
+ * random offset u in [0, 1) grid steps and truncate -- with u taken at the
+ * midpoint of the 16-bit random value's interval, u = (r16 + 1/2) / 2^16.
+ * With lo the largest grid magnitude <= |v|, hi the next one and
+ * frac = (|v| - lo) / (hi - lo): round up iff frac + u >= 1.  Then
+ * P(up) = floor(frac * 2^16 + 1/2) / 2^16, within 2^-17 of frac either
+ * way.  |v| >= 6 saturates to 6; a value on the grid (frac = 0) never moves
+ * because u < 1. */
 uint8_t oracle_e2m1_sr(float v, uint32_t r16)
 {
     double a = fabs((double)v);
@@ -117,9 +121,9 @@ uint8_t oracle_e2m1_sr(float v, uint32_t r16)
     for (int j = 0; j < 8; ++j)
         if (E2M1_MAG[j] <= a) lo = j;
     double step = E2M1_MAG[lo + 1] - E2M1_MAG[lo];
-    double frac = (a - E2M1_MAG[lo]) / step;
-    double u = (double)(r16 & 0xFFFFu) / 65536.0;
-    int code = (u < frac) ? lo + 1 : lo;
+    double frac = (a - E2M1_MAG[lo]) / step;          /* exact: step is a power of two */
+    double u = ((double)(r16 & 0xFFFFu) + 0.5) / 65536.0;
+    int code = (frac >= 1.0 - u) ? lo + 1 : lo;       /* frac + u >= 1, both sides exact */
     return (uint8_t)(sign | code);
 }
 

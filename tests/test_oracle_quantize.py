@@ -289,10 +289,11 @@ def test_sr_counter_is_output_layout_index(axis):
     x = y if axis == 1 else np.ascontiguousarray(y.T)
     q = oracle.quantize(x, axis=axis, rounding=oracle.SR, seed=seed, offset=off)
     c = _codes_unpacked(q)
-    frac = float(np.float32(3.2)) - 3.0
+    frac = Fraction(float(np.float32(3.2))) - 3
     for o in range(outer):
         for k in range(K):
             if k % 16 == 0:
                 continue
             r = oracle.sr_bits(seed, off, o * K + k)
-            assert c[o, k] == (6 if r / 65536 < frac else 5), (o, k)
+            up = frac + (Fraction(r) + Fraction(1, 2)) / 65536 >= 1
+            assert c[o, k] == (6 if up else 5), (o, k)

@@ -6,6 +6,7 @@ probability, the pages' worked example and unbiasedness statistics.
 """
 import math
 import os
+from fractions import Fraction
 import shutil
 import subprocess
 
@@ -76,18 +77,51 @@ def _p_up_count(v, hi):
     return sum(oracle.e2m1_value(oracle.e2m1_sr(v, r)) == hi for r in range(65536))
 
 
-@pytest.mark.parametrize("v", [0.1, 0.3, 0.74, 1.2, 1.7, 2.9, 3.2, 4.5, 5.99])
+@pytest.mark.parametrize("v", [0.1, 0.3, 0.74, 1.2, 1.7, 2.9, 3.2, 4.5, 5.99, 1.0000001, 5.9999995])
 def test_sr_probability_closed_form(v):
+    # Adding u = (r16 + 1/2) / 2^16 grid steps and truncating rounds up for
+    # exactly the r16 >= 2^16 (1 - frac) - 1/2, i.e. floor(frac 2^16 + 1/2)
+    # of the 2^16 values: P(up) is frac rounded to 16 bits (within 2^-17).
     v = float(np.float32(v))
     grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
     lo = max(g for g in grid if g <= v)
     hi = grid[grid.index(lo) + 1]
-    frac = (v - lo) / (hi - lo)
-    # exhaustive over the 16-bit random value: up iff r/2^16 < frac
-    assert _p_up_count(v, hi) == math.ceil(frac * 65536)
-    assert oracle.e2m1_value(oracle.e2m1_sr(v, 0xFFFF)) == lo
-    if frac > 0:
-        assert oracle.e2m1_value(oracle.e2m1_sr(v, 0)) == hi
+    frac = Fraction(v) - Fraction(lo)
+    frac /= Fraction(hi) - Fraction(lo)
+    count = _p_up_count(v, hi)
+    assert count == math.floor(frac * 65536 + Fraction(1, 2))
+    assert abs(Fraction(count, 65536) - frac) <= Fraction(1, 2 ** 17)
+    # the smallest offset (r16 = 0) rounds up only when frac >= 1 - 2^-17,
+    # the largest (r16 = 0xFFFF) whenever frac >= 2^-17
+    assert oracle.e2m1_value(oracle.e2m1_sr(v, 0)) == (hi if frac >= 1 - Fraction(1, 2 ** 17) else lo)
+    assert oracle.e2m1_value(oracle.e2m1_sr(v, 0xFFFF)) == (hi if frac >= Fraction(1, 2 ** 17) else lo)
+
+
+def test_sr_brute_force_add_and_truncate():
+    # The definition written as arithmetic on exact rationals: value / step +
+    # u, truncated, times step, over random values in every binade and
+    # random 16-bit draws.
+    rng = np.random.default_rng(17)
+    grid = [Fraction(g) for g in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    vals = np.concatenate([rng.uniform(0, 6.5, 3000), np.exp2(rng.uniform(-40, 2.6, 1000))]).astype(np.float32)
+    for v, r in zip(vals, rng.integers(0, 65536, vals.size)):
+        a = Fraction(float(v))
+        if a >= 6:
+            want = Fraction(6)
+        else:
+            lo = max(g for g in grid if g <= a)
+            hi = grid[grid.index(lo) + 1]
+            step = hi - lo
+            t = (a - lo) / step + (Fraction(int(r)) + Fraction(1, 2)) / 65536
+            want = lo + step * (1 if t >= 1 else 0)
+        assert Fraction(oracle.e2m1_value(oracle.e2m1_sr(float(v), int(r)))) == want, (float(v), int(r))
+
+
+def test_sr_tiny_values_stay_zero():
+    # |v| far below half a grid step: frac < 2^-17, so no draw rounds it up
+    for v in (1e-30, -1e-30, 2.0 ** -20, np.float32(1e-40)):
+        for r in (0, 1, 0x7FFF, 0xFFFF):
+            assert oracle.e2m1_value(oracle.e2m1_sr(float(v), r)) == 0.0
 
 
 def test_sr_worked_example_frequencies():
