@@ -18,10 +18,10 @@
 //  * the amax pass keeps four 16-byte loads in flight per thread;
 //  * the encode pass walks the tensor in the opposite order of the amax
 //    pass, so its first part is still resident in the 256 MB MALL;
-//  * axis 0 (K runs down the columns; the output is the transpose) stages a
-//    512-row x 32-column tile in LDS with coalesced 16-byte loads, so each
-//    thread reads its column's 16-element blocks from LDS and the codes and
-//    scales of one output row are written as contiguous runs.
+//  * axis 0 (K runs down the columns; the output is the transpose) gives
+//    each thread two adjacent columns and four consecutive blocks: rows are
+//    read as 1 KB contiguous runs per workgroup and each output row gets 32
+//    code bytes and 4 scale bytes from one thread.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -117,75 +117,46 @@ __global__ void __launch_bounds__(kQT) k_amax_rht_rows(const T *x, int64_t nchun
   block_max_atomic(m, amax_bits);
 }
 
-// ------------------------------------------------- axis-0 LDS tiles ----
+// ------------------------------------------------------- axis 0 ----
 //
-// A tile is 32 columns x kTileBlocks 16-row blocks of the input (512 rows).
-// LDS holds it row-major as 32-bit words with one 4-word pad after every
-// 16 rows, so that the 16 threads reading the same row offset of 16
-// different blocks hit 16 different bank groups.  Thread t handles the
-// column pair cp = t / 16 (columns 2cp, 2cp+1) and blocks g = t % 16 and
-// g + 16: sixteen consecutive threads then write one output row's 16
-// consecutive code words (128 bytes) and scales.
-constexpr int kTileCols = 32;
-constexpr int kTileBlocks = 32;
-constexpr int kTileRows = 16 * kTileBlocks;
+// K runs down the columns.  A thread owns kCPT adjacent columns (two bf16
+// columns share one 4-byte load, f32 takes one) and kNBT consecutive
+// 16-row blocks, so a wave reads 256 contiguous bytes of each row and a
+// workgroup 1 KB, and each output row (= input column) receives kNBT code
+// words (32 bytes) and kNBT scale bytes from one thread.  Grid: x over
+// column groups of 256 * kCPT, y over groups of kNBT blocks.
+constexpr int kNBT = 4;
 
 template <typename T>
-struct ColTile {
-  static constexpr int kWordsPerRow = kTileCols * (int)sizeof(T) / 4;   // 16 (bf16) or 32 (f32)
-  static constexpr int kWords = kTileRows * kWordsPerRow + 4 * kTileBlocks;
-  __device__ static __forceinline__ int word(int row, int w) { return row * kWordsPerRow + w + 4 * (row >> 4); }
+struct ColPairs {
+  static constexpr int kCPT = 4 / (int)sizeof(T);   // columns per thread
 };
 
-// Load rows [r0, r0 + 512) x columns [c0, c0 + 32) of x into the LDS tile;
-// positions outside the matrix read as zero.
+// The 16 values of block kb of columns c .. c + kCPT - 1 (binary32; columns
+// past `cols` read as zero).  `fast`: one aligned 4-byte load per row.
 template <typename T>
-__device__ __forceinline__ void load_col_tile(const T *x, int64_t rows, int64_t cols, int64_t r0, int64_t c0,
-                                              uint32_t *tile) {
-  using Tl = ColTile<T>;
-  constexpr int kVecPerRow = Tl::kWordsPerRow / 4;   // 16-byte vectors per tile row
-  constexpr int kVecs = kTileRows * kVecPerRow;
-  const bool vec_ok = (c0 + kTileCols <= cols) && ((cols * (int64_t)sizeof(T)) % 16 == 0);
-  if (vec_ok) {
-#pragma unroll 4
-    for (int u = threadIdx.x; u < kVecs; u += kQT) {
-      const int row = u / kVecPerRow, q = u % kVecPerRow;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r0 + row < rows) v = *reinterpret_cast<const uint4 *>(x + (r0 + row) * cols + c0 + q * (16 / sizeof(T)));
-      *reinterpret_cast<uint4 *>(tile + Tl::word(row, 4 * q)) = v;
+__device__ __forceinline__ void load_col_block(const T *x, int64_t cols, int64_t kb, int64_t c, bool fast,
+                                               float (*y)[16]) {
+  constexpr int CPT = ColPairs<T>::kCPT;
+  const T *p = x + 16 * kb * cols + c;
+  if (fast) {
+    uint32_t w[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = *reinterpret_cast<const uint32_t *>(p + j * cols);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (CPT == 2) {
+        y[0][j] = bf16_lo(w[j]);
+        y[1][j] = bf16_hi(w[j]);
+      } else {
+        y[0][j] = __uint_as_float(w[j]);
+      }
     }
   } else {
-    constexpr int kPerWord = 4 / (int)sizeof(T);
-    for (int u = threadIdx.x; u < kTileRows * Tl::kWordsPerRow; u += kQT) {
-      const int row = u / Tl::kWordsPerRow, w = u % Tl::kWordsPerRow;
-      uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < kPerWord; ++e) {
-        const int64_t c = c0 + w * kPerWord + e;
-        if (r0 + row < rows && c < cols) {
-          const T v = x[(r0 + row) * cols + c];
-          word |= (uint32_t)__builtin_bit_cast(typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type, v)
-                  << (16 * e * (sizeof(T) == 2));
-        }
-      }
-      tile[Tl::word(row, w)] = word;
-    }
-  }
-}
-
-// The 16 values of column cc (0..31) in tile block blk, as binary32.
-template <typename T>
-__device__ __forceinline__ void tile_block(const uint32_t *tile, int blk, int cc, float *y) {
-  using Tl = ColTile<T>;
+    for (int e = 0; e < CPT; ++e)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int row = 16 * blk + j;
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t w = tile[Tl::word(row, cc >> 1)];
-      y[j] = (cc & 1) ? bf16_hi(w) : bf16_lo(w);
-    } else {
-      y[j] = __uint_as_float(tile[Tl::word(row, cc)]);
-    }
+      for (int j = 0; j < 16; ++j) y[e][j] = (c + e < cols) ? to_f32<T>(p[j * cols + e]) : 0.0f;
   }
 }
 
@@ -193,20 +164,22 @@ __device__ __forceinline__ void tile_block(const uint32_t *tile, int blk, int cc
 template <typename T>
 __global__ void __launch_bounds__(kQT) k_amax_rht_cols(const T *x, int64_t rows, int64_t cols, uint32_t sign_mask,
                                                       uint32_t *amax_bits) {
-  __shared__ uint32_t tile[ColTile<T>::kWords];
-  const int64_t c0 = (int64_t)blockIdx.x * kTileCols, r0 = (int64_t)blockIdx.y * kTileRows;
-  load_col_tile<T>(x, rows, cols, r0, c0, tile);
-  __syncthreads();
-  const int cp = threadIdx.x >> 4, g = threadIdx.x & 15;
+  constexpr int CPT = ColPairs<T>::kCPT;
+  const int64_t c = ((int64_t)blockIdx.x * kQT + threadIdx.x) * CPT;
+  const int64_t nkb = rows / 16, kb0 = (int64_t)blockIdx.y * kNBT;
+  const bool fast = (c + CPT <= cols) && (CPT == 1 || (cols % 2) == 0);
   uint32_t m = 0;
+  if (c < cols) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+    for (int i = 0; i < kNBT; ++i) {
+      if (kb0 + i >= nkb) break;
+      float y[CPT][16];
+      load_col_block<T>(x, cols, kb0 + i, c, fast, y);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      float y[16];
-      tile_block<T>(tile, g + 16 * h, 2 * cp + e, y);   // zero rows/columns stay zero
-      rht16(y, sign_mask);
-      m = max(m, absmax_bits16(y));
+      for (int e = 0; e < CPT; ++e) {
+        rht16(y[e], sign_mask);
+        m = max(m, absmax_bits16(y[e]));
+      }
     }
   }
   block_max_atomic(m, amax_bits);
@@ -236,38 +209,57 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
   }
 }
 
-// axis 0: one 512-row x 32-column tile per workgroup (see ColTile).  Output
-// row o = column, block kb = 16-row group; the tiles are visited in reverse
-// order of the amax pass.
+// axis 0: output row o = input column, block kb = 16-row group; the blocks
+// are visited in reverse order of the amax pass.
 template <typename T, bool SR, bool RHT>
 __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, int64_t cols, uint32_t sign_mask,
                                                    uint64_t seed, uint64_t offset, float *meta, uint2 *codes,
                                                    uint8_t *scales) {
-  __shared__ uint32_t tile[ColTile<T>::kWords];
+  constexpr int CPT = ColPairs<T>::kCPT;
   const float amax = meta[0];
   const TensorScales ts = tensor_scales(amax);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) meta[1] = ts.g;
-  const int64_t c0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * kTileCols;
-  const int64_t r0 = (int64_t)(gridDim.y - 1 - blockIdx.y) * kTileRows;
-  load_col_tile<T>(x, rows, cols, r0, c0, tile);
-  __syncthreads();
-  const int64_t nkb = rows / 16, kb0 = r0 / 16;
-  const int cp = threadIdx.x >> 4, g = threadIdx.x & 15;
+  const int64_t c = ((int64_t)(gridDim.x - 1 - blockIdx.x) * kQT + threadIdx.x) * CPT;
+  const int64_t nkb = rows / 16, kb0 = (int64_t)(gridDim.y - 1 - blockIdx.y) * kNBT;
+  if (c >= cols) return;
+  const bool fast = (c + CPT <= cols) && (CPT == 1 || (cols % 2) == 0);
+  const int nb = (int)(nkb - kb0 < kNBT ? nkb - kb0 : kNBT);
+  uint2 cw[CPT][kNBT];
+  uint32_t sc[CPT] = {};
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int64_t o = c0 + 2 * cp + e;
+  for (int i = 0; i < kNBT; ++i) {
+    if (i >= nb) break;
+    float y[CPT][16];
+    load_col_block<T>(x, cols, kb0 + i, c, fast, y);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t kb = kb0 + g + 16 * h;
-      if (o >= cols || kb >= nkb) continue;
-      float y[16];
-      tile_block<T>(tile, g + 16 * h, 2 * cp + e, y);
-      if (RHT) rht16(y, sign_mask);
+    for (int e = 0; e < CPT; ++e) {
+      if (RHT) rht16(y[e], sign_mask);
       float m;
-      const uint32_t S = block_scale(absmax_bits16(y), ts, &m);
-      const int64_t blk = o * nkb + kb;   // block index in the [outer][K/16] layout
-      codes[blk] = encode16<SR>(y, m, (uint64_t)blk, seed, offset);
-      scales[blk] = (uint8_t)S;
+      const uint32_t S = block_scale(absmax_bits16(y[e]), ts, &m);
+      const int64_t blk = (c + e) * nkb + kb0 + i;   // block index in the [outer][K/16] layout
+      cw[e][i] = encode16<SR>(y[e], m, (uint64_t)blk, seed, offset);
+      sc[e] |= S << (8 * i);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+    if (c + e >= cols) break;
+    const int64_t blk0 = (c + e) * nkb + kb0;
+    if (nb == kNBT && (blk0 % 2) == 0) {
+      uint4 *dst = reinterpret_cast<uint4 *>(codes + blk0);
+      dst[0] = make_uint4(cw[e][0].x, cw[e][0].y, cw[e][1].x, cw[e][1].y);
+      dst[1] = make_uint4(cw[e][2].x, cw[e][2].y, cw[e][3].x, cw[e][3].y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kNBT; ++i)
+        if (i < nb) codes[blk0 + i] = cw[e][i];
+    }
+    if (nb == kNBT && (blk0 % 4) == 0) {
+      *reinterpret_cast<uint32_t *>(scales + blk0) = sc[e];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kNBT; ++i)
+        if (i < nb) scales[blk0 + i] = (uint8_t)(sc[e] >> (8 * i));
     }
   }
 }
@@ -334,8 +326,9 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
   hipLaunchKernelGGL(k_meta_init, dim3(1), dim3(64), 0, stream, meta);
   if (n == 0) return hipGetLastError();
   const bool bf16 = (x_dtype == 1);
-  const dim3 tiles((unsigned)((cols + kTileCols - 1) / kTileCols), (unsigned)((rows + kTileRows - 1) / kTileRows));
-  if (axis == 0 && tiles.y > 65535u) return hipErrorInvalidValue;
+  const int64_t cpt = bf16 ? 2 : 1;
+  const dim3 tiles((unsigned)((cols + kQT * cpt - 1) / (kQT * cpt)), (unsigned)((rows / 16 + kNBT - 1) / kNBT));
+  if (axis == 0 && (rows / 16 + kNBT - 1) / kNBT > 65535) return hipErrorInvalidValue;
   // pass 1: amax
   if (!rht) {
     const int64_t n16 = n * (bf16 ? 2 : 4) / 16;
