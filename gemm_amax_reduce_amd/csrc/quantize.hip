@@ -15,7 +15,8 @@
 // zeroes meta, (2) an amax kernel (integer max of |x| bit patterns, wave
 // reduction, one atomicMax per workgroup), (3) the encode kernel, which
 // re-reads the input.  Both passes are HBM-bound:
-//  * the amax pass keeps four 16-byte loads in flight per thread;
+//  * the amax pass streams one contiguous chunk per workgroup with four
+//    16-byte loads in flight per thread;
 //  * the encode pass walks the tensor in the opposite order of the amax
 //    pass, so its first part is still resident in the 256 MB MALL;
 //  * axis 0 (K runs down the columns; the output is the transpose) gives
@@ -39,7 +40,12 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   return v;
 }
 
-// Reduce a per-thread max over the workgroup and fold it into *dst.
+// Reduce a per-thread max over the workgroup and fold it into *dst.  Atomics
+// on one address serialise in L2 (thousands of workgroups each issuing one
+// cost tens of microseconds), so the current value is read first (relaxed,
+// device scope: not from a stale L1 line) and the atomic is issued only when
+// this workgroup can raise it.  The result is the same maximum: a skipped
+// update was already dominated by a value in *dst, and *dst only grows.
 __device__ __forceinline__ void block_max_atomic(uint32_t v, uint32_t *dst) {
   __shared__ uint32_t part[kQT / 64];
   v = wave_max(v);
@@ -50,7 +56,8 @@ __device__ __forceinline__ void block_max_atomic(uint32_t v, uint32_t *dst) {
     uint32_t m = part[0];
 #pragma unroll
     for (int i = 1; i < kQT / 64; ++i) m = max(m, part[i]);
-    if (m) atomicMax(dst, m);
+    const uint32_t cur = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m > cur) atomicMax(dst, m);
   }
 }
 
@@ -78,37 +85,42 @@ template <> __device__ __forceinline__ uint32_t vec_absmax<float>(uint4 v) {
 // --------------------------------------------------------------- amax ----
 
 // Flat amax over n16 16-byte vectors (no transform; the axis does not
-// matter).  Four loads in flight per thread per iteration.
+// matter).  Each workgroup streams one contiguous chunk with four loads in
+// flight per thread (measured on MI355X: contiguous chunks per workgroup
+// read ~15 % faster than a grid-wide stride, which spreads every wave's
+// accesses over the whole tensor).
 template <typename T>
-__global__ void __launch_bounds__(kQT) k_amax_flat(const uint4 *x, int64_t n16, uint32_t *amax_bits) {
+__global__ void __launch_bounds__(kQT) k_amax_flat(const uint4 *x, int64_t n16, int64_t per_wg, uint32_t *amax_bits) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kQT;
-  int64_t i = (int64_t)blockIdx.x * kQT + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = x[i], v1 = x[i + stride], v2 = x[i + 2 * stride], v3 = x[i + 3 * stride];
+  const int64_t beg = (int64_t)blockIdx.x * per_wg;
+  const int64_t end = beg + per_wg < n16 ? beg + per_wg : n16;
+  int64_t i = beg + threadIdx.x;
+  for (; i + 3 * kQT < end; i += 4 * kQT) {
+    const uint4 v0 = x[i], v1 = x[i + kQT], v2 = x[i + 2 * kQT], v3 = x[i + 3 * kQT];
     m = max(max(m, vec_absmax<T>(v0)), max(vec_absmax<T>(v1), max(vec_absmax<T>(v2), vec_absmax<T>(v3))));
   }
-  for (; i < n16; i += stride) m = max(m, vec_absmax<T>(x[i]));
+  for (; i < end; i += kQT) m = max(m, vec_absmax<T>(x[i]));
   block_max_atomic(m, amax_bits);
 }
 
-// amax of the transformed tensor, axis 1: one 16-chunk of a row per thread
-// and iteration, two chunks in flight.
+// amax of the transformed tensor, axis 1: 16-chunks of rows, one contiguous
+// range of chunks per workgroup, two chunks in flight per thread.
 template <typename T>
-__global__ void __launch_bounds__(kQT) k_amax_rht_rows(const T *x, int64_t nchunks, uint32_t sign_mask,
+__global__ void __launch_bounds__(kQT) k_amax_rht_rows(const T *x, int64_t nchunks, int64_t per_wg, uint32_t sign_mask,
                                                       uint32_t *amax_bits) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kQT;
-  int64_t c = (int64_t)blockIdx.x * kQT + threadIdx.x;
-  for (; c + stride < nchunks; c += 2 * stride) {
+  const int64_t beg = (int64_t)blockIdx.x * per_wg;
+  const int64_t end = beg + per_wg < nchunks ? beg + per_wg : nchunks;
+  int64_t c = beg + threadIdx.x;
+  for (; c + kQT < end; c += 2 * kQT) {
     float y0[16], y1[16];
     Load16<T>::run(x + 16 * c, y0);
-    Load16<T>::run(x + 16 * (c + stride), y1);
+    Load16<T>::run(x + 16 * (c + kQT), y1);
     rht16(y0, sign_mask);
     rht16(y1, sign_mask);
     m = max(m, max(absmax_bits16(y0), absmax_bits16(y1)));
   }
-  for (; c < nchunks; c += stride) {
+  for (; c < end; c += kQT) {
     float y[16];
     Load16<T>::run(x + 16 * c, y);
     rht16(y, sign_mask);
@@ -332,14 +344,16 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
   // pass 1: amax
   if (!rht) {
     const int64_t n16 = n * (bf16 ? 2 : 4) / 16;
-    unsigned g = grid_for(n16, kQT * 4, 2048);
-    if (bf16) hipLaunchKernelGGL(k_amax_flat<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, amax_bits);
-    else hipLaunchKernelGGL(k_amax_flat<float>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, amax_bits);
+    const unsigned g = grid_for(n16, kQT * 4, 1024);
+    const int64_t per = (n16 + g - 1) / g;
+    if (bf16) hipLaunchKernelGGL(k_amax_flat<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits);
+    else hipLaunchKernelGGL(k_amax_flat<float>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits);
   } else if (axis == 1) {
     const int64_t nch = n / 16;
-    unsigned g = grid_for(nch, kQT * 2, 4096);
-    if (bf16) hipLaunchKernelGGL(k_amax_rht_rows<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint16_t *)x, nch, sign_mask, amax_bits);
-    else hipLaunchKernelGGL(k_amax_rht_rows<float>, dim3(g), dim3(kQT), 0, stream, (const float *)x, nch, sign_mask, amax_bits);
+    const unsigned g = grid_for(nch, kQT * 2, 2048);
+    const int64_t per = (nch + g - 1) / g;
+    if (bf16) hipLaunchKernelGGL(k_amax_rht_rows<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint16_t *)x, nch, per, sign_mask, amax_bits);
+    else hipLaunchKernelGGL(k_amax_rht_rows<float>, dim3(g), dim3(kQT), 0, stream, (const float *)x, nch, per, sign_mask, amax_bits);
   } else {
     if (bf16) hipLaunchKernelGGL(k_amax_rht_cols<uint16_t>, tiles, dim3(kQT), 0, stream, (const uint16_t *)x, rows, cols, sign_mask, amax_bits);
     else hipLaunchKernelGGL(k_amax_rht_cols<float>, tiles, dim3(kQT), 0, stream, (const float *)x, rows, cols, sign_mask, amax_bits);
