@@ -34,8 +34,10 @@
 // consecutive K positions 16*ks + 8*h .. +7 of K step ks, for A and B alike,
 // which is the operand layout the MFMA sums over.
 //
-// Grid: one workgroup per tile (the launcher uses BN = 256; a 256 x 320
-// tile needs 320 accumulators per lane, more than the 256 AGPRs the
+// Grid: one workgroup per tile.  The launcher covers most columns with
+// 256 x 256 tiles and the remainder with 256 x 128 tiles in the same launch,
+// so the tile count fills whole rounds of the CUs (a single 256 x 320 tile
+// would need 320 accumulators per lane, more than the 256 AGPRs the
 // compiler keeps MFMA accumulators in).  Workgroups are dealt round-robin
 // to the eight XCDs (pid % 8); the tile index is remapped so each XCD works
 // on a contiguous range of tiles, ordered in groups of 8 tile rows, so that
@@ -43,6 +45,7 @@
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace nvfp4 {
@@ -107,14 +110,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// One 256 x BN output tile: workgroup `pid` of the tiles of C[M][N] = A.B^T
+// (B, C and N already restricted to this tile width's column range).
 template <bool OUT_BF16, bool SCALE16, int BN, int PF>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
-             const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
-             int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc) {
+__device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t *__restrict__ A,
+                                          const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
+                                          const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                                          const float *__restrict__ metaB, int64_t M, int64_t N, int64_t K,
+                                          void *__restrict__ C, int64_t ldc) {
   using Cfg = TileCfg<BN>;
   constexpr int NB = Cfg::kNB, NS = Cfg::kSlots;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg::kStage];
 
   // The wave index is uniform across a wave; readfirstlane tells the
   // compiler so, which keeps every per-slot choice (A or B view, the
@@ -126,7 +131,6 @@ k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
   // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
-  const int pid = blockIdx.x;
   const int xcd = pid % kXcds, local = pid / kXcds;
   const int q = ntiles / kXcds, r = ntiles % kXcds;
   const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
@@ -280,8 +284,10 @@ k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
         // A fragment i of the next K step replaces the one just consumed.
         if (ks + 1 < kKSteps) read_a(cur, ks + 1, i);
         const int u = 4 * ks + i;       // decode unit: chunk u/4, word u%4
-        decode_word(dec, u >> 2, u & 3, nxt);
-        if ((u & 3) == 3) load_chunk(dec, u >> 2, kload, Full{});
+        if ((u >> 2) < NS) {
+          decode_word(dec, u >> 2, u & 3, nxt);
+          if ((u & 3) == 3) load_chunk(dec, u >> 2, kload, Full{});
+        }
         if (NS > 4 && (u & 3) == 2 && last_slot) {   // the fifth chunk, one word per K step
           decode_word(dec, 4, ks, nxt);
           if (ks == 3) load_chunk(dec, 4, kload, Full{});
@@ -350,6 +356,26 @@ k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
   }
 }
 
+// The GEMM kernel: workgroups [0, n_big) compute the 256 x 256 tiles of
+// columns [0, n1), the others the 256 x 128 tiles of columns [n1, N).  The
+// branch is uniform per workgroup; LDS is sized for the larger tile.
+template <bool OUT_BF16, bool SCALE16>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
+             const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
+             int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc, int n_big, int64_t n1) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TileCfg<256>::kStage];
+  static_assert(TileCfg<128>::kStage <= TileCfg<256>::kStage, "LDS sized for the wide tile");
+  const int pid = blockIdx.x;
+  if (pid < n_big) {
+    gemm_tile<OUT_BF16, SCALE16, 256, 2>(smem, pid, A, SA, metaA, B, SB, metaB, M, n1, K, C, ldc);
+  } else {
+    using OutT = typename std::conditional<OUT_BF16, uint16_t, float>::type;
+    gemm_tile<OUT_BF16, SCALE16, 128, 2>(smem, pid - n_big, A, SA, metaA, B + n1 * (K / 2), SB + n1 * (K / 16), metaB,
+                                         M, N - n1, K, reinterpret_cast<OutT *>(C) + n1, ldc);
+  }
+}
+
 __global__ void k_zero_c(void *C, int64_t M, int64_t N, int64_t ldc, int elem) {
   const int64_t total = M * N;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -359,25 +385,16 @@ __global__ void k_zero_c(void *C, int64_t M, int64_t N, int64_t ldc, int elem) {
   }
 }
 
-template <int BN, int PF>
-hipError_t launch_bn(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_meta, const uint8_t *b_codes,
-                     const uint8_t *b_scales, const float *b_meta, int64_t M, int64_t N, int64_t K, void *c,
-                     int c_dtype, int64_t ldc, hipStream_t stream) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  dim3 grid((unsigned)tiles);
-  // 16-bit scale loads need an even number of scales per row (K % 32 == 0).
-  const bool s16 = (K % 32) == 0;
-#define NVFP4_GEMM_LAUNCH(OB, S16)                                                                              \
-  hipLaunchKernelGGL((k_gemm_nvfp4<OB, S16, BN, PF>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, \
-                     b_codes, b_scales, b_meta, M, N, K, c, ldc)
-  if (c_dtype == 0) {
-    if (s16) NVFP4_GEMM_LAUNCH(false, true); else NVFP4_GEMM_LAUNCH(false, false);
-  } else {
-    if (s16) NVFP4_GEMM_LAUNCH(true, true); else NVFP4_GEMM_LAUNCH(true, false);
-  }
-#undef NVFP4_GEMM_LAUNCH
-  return hipGetLastError();
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 }  // namespace
@@ -393,8 +410,40 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
     return hipGetLastError();
   }
   // The buffer views address one tile's rows with 32-bit offsets.
-  if ((int64_t)320 * (K / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  return launch_bn<256, 2>(a_codes, a_scales, a_meta, b_codes, b_scales, b_meta, M, N, K, c, c_dtype, ldc, stream);
+  if ((int64_t)BM * (K / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  // Balance the grid over the CUs.  Columns [0, n1) get 256 x 256 tiles and
+  // the rest 256 x 128 tiles (half the work per tile; their per-flop cost is
+  // taken as 1.1x); n1 minimises the modelled time
+  //   rounds(256-wide tiles) + 0.55 * rounds(128-wide tiles),
+  // rounds(t) = ceil(t / CUs).  The fprop, dgrad and wgrad layers would
+  // otherwise run 1.25, 2.5 and 6.25 rounds of 256 x 256 tiles as 2, 3 and 7.
+  // Both tile widths run in one launch; every output element is computed by
+  // exactly one workgroup.
+  const int64_t cus = device_cus();
+  const int64_t tm = (M + BM - 1) / BM, tn = (N + 255) / 256;
+  auto rounds = [&](int64_t t) { return (t + cus - 1) / cus; };
+  int64_t best_n1 = N;
+  double best = (double)rounds(tm * tn);
+  for (int64_t t1 = 0; t1 < tn; ++t1) {
+    const int64_t n1 = t1 * 256, rest = (N - n1 + 127) / 128;
+    const double cost = (double)rounds(tm * t1) + 0.55 * (double)rounds(tm * rest);
+    if (cost < best - 1e-9) { best = cost; best_n1 = n1; }
+  }
+  const int64_t n_big = tm * (best_n1 / 256), n_small = tm * ((N - best_n1 + 127) / 128);
+  if (n_big + n_small > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(n_big + n_small));
+  // 16-bit scale loads need an even number of scales per row (K % 32 == 0).
+  const bool s16 = (K % 32) == 0;
+#define NVFP4_GEMM_LAUNCH(OB, S16)                                                                          \
+  hipLaunchKernelGGL((k_gemm_nvfp4<OB, S16>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, \
+                     b_codes, b_scales, b_meta, M, N, K, c, ldc, (int)n_big, best_n1)
+  if (c_dtype == 0) {
+    if (s16) NVFP4_GEMM_LAUNCH(false, true); else NVFP4_GEMM_LAUNCH(false, false);
+  } else {
+    if (s16) NVFP4_GEMM_LAUNCH(true, true); else NVFP4_GEMM_LAUNCH(true, false);
+  }
+#undef NVFP4_GEMM_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4
