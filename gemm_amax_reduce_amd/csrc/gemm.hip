@@ -59,6 +59,11 @@ constexpr int kKSteps = BK / 16;                   // 4 MFMA K steps per stage
 constexpr int kGroupM = 8;                         // tile rows per L2 group
 constexpr int kXcds = 8;
 constexpr int kCodeLoadPolicy = 1;                // buffer-load cache policy bits: sc0
+// Where the decode takes the block scales from: per stage and chunk, one
+// byte load each (any K), one 16-bit load (K % 32 == 0), or from 4-stage
+// scale groups staged in LDS (K % 64 == 0, 4-byte aligned scale arrays).
+constexpr int kScalesU8 = 0, kScalesU16 = 1, kScalesLds = 2;
+constexpr int kScaleGroupBytes = 2 * 256 * 16;      // one group: 512 tile rows x 16 bytes
 
 template <int BN>
 struct TileCfg {
@@ -112,8 +117,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // One 256 x BN output tile: workgroup `pid` of the tiles of C[M][N] = A.B^T
 // (B, C and N already restricted to this tile width's column range).
-template <bool OUT_BF16, bool SCALE16, int BN, int PF>
-__device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t *__restrict__ A,
+template <bool OUT_BF16, int SCALES, int BN, int PF>
+__device__ __forceinline__ void gemm_tile(uint8_t *smem, uint8_t *sbuf, int pid, const uint8_t *__restrict__ A,
                                           const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
                                           const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
                                           const float *__restrict__ metaB, int64_t M, int64_t N, int64_t K,
@@ -183,9 +188,9 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
     // 32 KB vector L1 until the next stage, so L1 allocation only multiplies
     // the L2 -> L1 traffic; measured 12-20 % faster than the default policy.
     st.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff_code, so_c, kCodeLoadPolicy));
-    if constexpr (SCALE16) {
+    if constexpr (SCALES == kScalesU16) {
       st.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_scale, so_s, 0);
-    } else {  // a row's scales may start at an odd address
+    } else if constexpr (SCALES == kScalesU8) {  // a row's scales may start at an odd address
       st.s[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, voff_scale, so_s, 0) |
                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, voff_scale, so_s + 1, 0) << 8);
     }
@@ -196,7 +201,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
       st.c[j].y &= keep_lo;
       st.c[j].z &= keep_hi;
       st.c[j].w &= keep_hi;
-      st.s[j] &= (keep_lo & 0xFFu) | (keep_hi & 0xFF00u);
+      if constexpr (SCALES != kScalesLds) st.s[j] &= (keep_lo & 0xFFu) | (keep_hi & 0xFF00u);
     }
   };
   auto load_stage = [&](StageRegs<NS> &st, int64_t k0, auto tail) {
@@ -205,20 +210,65 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
       if (j < NS - 1 || last_slot) load_chunk(st, j, k0, tail);
   };
 
+  // The two E4M3 block scales of chunk j for stage t (the chunk's 32 K
+  // positions span two 16-blocks), as an f16 pair.  With SCALES ==
+  // kScalesLds they come from the workgroup's LDS scale groups: group gg
+  // holds stages 4gg .. 4gg+3, 16 bytes per tile row (A rows 0..255, B rows
+  // 256..), in buffer gg % 2.
+  auto chunk_scales = [&](const StageRegs<NS> &st, int j, int t) {
+    uint32_t sc;
+    if constexpr (SCALES == kScalesLds) {
+      const uint32_t row = (is_b_slot(j) ? BM : 0) + base_row + slot_rows(j);
+      sc = *reinterpret_cast<const uint16_t *>(sbuf + ((t >> 2) & 1) * kScaleGroupBytes + row * 16 + 4 * (t & 3) + 2 * c);
+    } else {
+      sc = st.s[j];
+    }
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+  };
   // Decode word wd (8 codes) of chunk j into the LDS stage buffer: word wd
   // goes to K step 2c + wd/2, lane slot l32 + 32*(wd%2).
-  auto decode_word = [&](const StageRegs<NS> &st, int j, int wd, uint8_t *buf) {
-    const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.s[j], 1.0f, false);
+  auto decode_word = [&](const StageRegs<NS> &st, int j, int wd, half2_t s2, uint8_t *buf) {
     const uint32_t w = wd == 0 ? st.c[j].x : wd == 1 ? st.c[j].y : wd == 2 ? st.c[j].z : st.c[j].w;
     uint8_t *dst = buf + lds_base + j * (4 * kKSteps * kFrag) + (wd >> 1) * kFrag + (wd & 1) * (32 * 16);
     *reinterpret_cast<u32x4 *>(dst) = decode8(w, s2, wd >= 2);
   };
-  auto store_stage = [&](const StageRegs<NS> &st, uint8_t *buf) {
+  auto store_stage = [&](const StageRegs<NS> &st, int t, uint8_t *buf) {
 #pragma unroll
     for (int j = 0; j < NS; ++j)
-      if (j < NS - 1 || last_slot)
+      if (j < NS - 1 || last_slot) {
+        const half2_t s2 = chunk_scales(st, j, t);
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) decode_word(st, j, wd, buf);
+        for (int wd = 0; wd < 4; ++wd) decode_word(st, j, wd, s2, buf);
+      }
+  };
+
+  // Scale groups (SCALES == kScalesLds): thread tid loads 16 bytes (the
+  // scales of 4 stages) of A row tid and of B row tid -- one 16-byte load
+  // per row per 4 stages instead of a 2-byte load per chunk per stage -- and
+  // writes them to LDS two stages later.  Scales past K read as zero.
+  u32x4 sgr[2];
+  auto load_sgroup = [&](int gg) {
+    const uint32_t so = (uint32_t)(16 * gg);
+    sgr[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(va.scales, tid * row_scales, so, 0));
+    sgr[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vb.scales, tid * row_scales, so, 0));
+  };
+  // The K tail is masked here, when the loaded data is consumed, so the
+  // loads stay in flight for two stages.
+  auto store_sgroup = [&](int gg) {
+    const int64_t valid = (int64_t)row_scales - 16 * (int64_t)gg;   // valid bytes of this group
+    if (valid < 16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int64_t nb = valid - 4 * q4;
+          const uint32_t keep = nb >= 4 ? ~0u : nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u);
+          sgr[h][q4] &= keep;
+        }
+    }
+    uint8_t *dst = sbuf + (gg & 1) * kScaleGroupBytes;
+    *reinterpret_cast<u32x4 *>(dst + tid * 16) = sgr[0];
+    *reinterpret_cast<u32x4 *>(dst + (BM + tid) * 16) = sgr[1];
   };
 
   float16_t acc[4][NB];
@@ -240,8 +290,13 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   // decoded, PF stages later.
   static_assert(PF == 1 || PF == 2, "prefetch depth");
   StageRegs<NS> st[PF];
+  if constexpr (SCALES == kScalesLds) {
+    load_sgroup(0);
+    store_sgroup(0);
+    __syncthreads();
+  }
   load_stage(st[0], 0, Tail{});
-  store_stage(st[0], smem);
+  store_stage(st[0], 0, smem);
   load_stage(st[1 % PF], BK, Tail{});
   if constexpr (PF == 2) load_stage(st[0], 2 * BK, Tail{});
   __syncthreads();
@@ -264,10 +319,15 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
     for (int j = 0; j < NB; ++j)
       bf_[j] = *reinterpret_cast<const half8_t *>(cur + b_frag0 + (j * kKSteps + ks) * kFrag);
   };
-  auto main_stage = [&](int s, StageRegs<NS> &dec) {
+  // `phase` = s % 4 (compile time): with LDS scale groups, phase 0 loads
+  // group s/4 + 1 and phase 2 writes it to LDS (the barrier ending that
+  // stage publishes it before stage 4(s/4 + 1) is decoded, in phase 3).
+  auto main_stage = [&](int s, StageRegs<NS> &dec, auto phase) {
+    constexpr int P = decltype(phase)::value;
     const uint8_t *cur = smem + (s & 1) * Cfg::kStage;
     uint8_t *nxt = smem + ((s & 1) ^ 1) * Cfg::kStage;
     const int64_t kload = (int64_t)(s + 1 + PF) * BK;
+    half2_t s2[NS];
 #pragma unroll
     for (int i = 0; i < 4; ++i) read_a(cur, 0, i);
     read_b(cur, 0, bf[0]);
@@ -285,23 +345,43 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
         if (ks + 1 < kKSteps) read_a(cur, ks + 1, i);
         const int u = 4 * ks + i;       // decode unit: chunk u/4, word u%4
         if ((u >> 2) < NS) {
-          decode_word(dec, u >> 2, u & 3, nxt);
+          if ((u & 3) == 0) s2[u >> 2] = chunk_scales(dec, u >> 2, s + 1);
+          decode_word(dec, u >> 2, u & 3, s2[u >> 2], nxt);
           if ((u & 3) == 3) load_chunk(dec, u >> 2, kload, Full{});
         }
         if (NS > 4 && (u & 3) == 2 && last_slot) {   // the fifth chunk, one word per K step
-          decode_word(dec, 4, ks, nxt);
+          if (ks == 0) s2[4] = chunk_scales(dec, 4, s + 1);
+          decode_word(dec, 4, ks, s2[4], nxt);
           if (ks == 3) load_chunk(dec, 4, kload, Full{});
+        }
+        if constexpr (SCALES == kScalesLds) {
+          if (P == 0 && u == 1) load_sgroup(s / 4 + 1);
+          if (P == 2 && u == 9) store_sgroup(s / 4 + 1);
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
 
   int s = 0;
-  for (; s + PF + 2 < nfull; s += 2) {   // the stages loaded here are all full
-    main_stage(s, st[1 % PF]);
-    main_stage(s + 1, st[0]);
+  if constexpr (SCALES == kScalesLds) {
+    static_assert(PF == 2, "the scale-group schedule assumes two register sets");
+    for (; s + PF + 4 < nfull; s += 4) {   // the code stages loaded here are all full
+      main_stage(s, st[1], P0{});
+      main_stage(s + 1, st[0], P1{});
+      main_stage(s + 2, st[1], P2{});
+      main_stage(s + 3, st[0], P3{});
+    }
+  } else {
+    for (; s + PF + 2 < nfull; s += 2) {   // the stages loaded here are all full
+      main_stage(s, st[1 % PF], P0{});
+      main_stage(s + 1, st[0], P1{});
+    }
   }
   // Tail: the last stages (loads may be partial or past K: zeros).
   for (; s < nk; ++s) {
@@ -319,11 +399,15 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[0][j], acc[i][j], 0, 0, 0);
     }
     if (PF == 2 && ((s + 1) & 1)) {
-      store_stage(st[1 % PF], nxt);
+      store_stage(st[1 % PF], s + 1, nxt);
       load_stage(st[1 % PF], (int64_t)(s + 1 + PF) * BK, Tail{});
     } else {
-      store_stage(st[0], nxt);
+      store_stage(st[0], s + 1, nxt);
       load_stage(st[0], (int64_t)(s + 1 + PF) * BK, Tail{});
+    }
+    if constexpr (SCALES == kScalesLds) {   // same schedule as the main loop
+      if ((s & 3) == 0) load_sgroup(s / 4 + 1);
+      if ((s & 3) == 2) store_sgroup(s / 4 + 1);
     }
     __syncthreads();
   }
@@ -358,21 +442,23 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
 
 // The GEMM kernel: workgroups [0, n_big) compute the 256 x 256 tiles of
 // columns [0, n1), the others the 256 x 128 tiles of columns [n1, N).  The
-// branch is uniform per workgroup; LDS is sized for the larger tile.
-template <bool OUT_BF16, bool SCALE16>
+// branch is uniform per workgroup; LDS is sized for the larger tile (two
+// 64 KB decoded stages and two 8 KB scale groups).
+template <bool OUT_BF16, int SCALES>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
              const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
              int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc, int n_big, int64_t n1) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TileCfg<256>::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TileCfg<256>::kStage + 2 * kScaleGroupBytes];
   static_assert(TileCfg<128>::kStage <= TileCfg<256>::kStage, "LDS sized for the wide tile");
+  uint8_t *sbuf = smem + 2 * TileCfg<256>::kStage;
   const int pid = blockIdx.x;
   if (pid < n_big) {
-    gemm_tile<OUT_BF16, SCALE16, 256, 2>(smem, pid, A, SA, metaA, B, SB, metaB, M, n1, K, C, ldc);
+    gemm_tile<OUT_BF16, SCALES, 256, 2>(smem, sbuf, pid, A, SA, metaA, B, SB, metaB, M, n1, K, C, ldc);
   } else {
     using OutT = typename std::conditional<OUT_BF16, uint16_t, float>::type;
-    gemm_tile<OUT_BF16, SCALE16, 128, 2>(smem, pid - n_big, A, SA, metaA, B + n1 * (K / 2), SB + n1 * (K / 16), metaB,
-                                         M, N - n1, K, reinterpret_cast<OutT *>(C) + n1, ldc);
+    gemm_tile<OUT_BF16, SCALES, 128, 2>(smem, sbuf, pid - n_big, A, SA, metaA, B + n1 * (K / 2), SB + n1 * (K / 16),
+                                        metaB, M, N - n1, K, reinterpret_cast<OutT *>(C) + n1, ldc);
   }
 }
 
@@ -432,16 +518,23 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
   const int64_t n_big = tm * (best_n1 / 256), n_small = tm * ((N - best_n1 + 127) / 128);
   if (n_big + n_small > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(n_big + n_small));
-  // 16-bit scale loads need an even number of scales per row (K % 32 == 0).
-  const bool s16 = (K % 32) == 0;
-#define NVFP4_GEMM_LAUNCH(OB, S16)                                                                          \
-  hipLaunchKernelGGL((k_gemm_nvfp4<OB, S16>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, \
+  // Scale path: 16-byte scale-group loads need K % 64 == 0 (a row's scales
+  // then start on a 4-byte boundary) and 4-byte aligned scale arrays; 16-bit
+  // per-stage loads need K % 32 == 0; otherwise single bytes.
+  const bool a4 = ((uintptr_t)a_scales % 4 == 0) && ((uintptr_t)b_scales % 4 == 0);
+  const int mode = (K % 64 == 0 && a4) ? kScalesLds : (K % 32 == 0 ? kScalesU16 : kScalesU8);
+#define NVFP4_GEMM_LAUNCH(OB, SM)                                                                          \
+  hipLaunchKernelGGL((k_gemm_nvfp4<OB, SM>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, \
                      b_codes, b_scales, b_meta, M, N, K, c, ldc, (int)n_big, best_n1)
-  if (c_dtype == 0) {
-    if (s16) NVFP4_GEMM_LAUNCH(false, true); else NVFP4_GEMM_LAUNCH(false, false);
-  } else {
-    if (s16) NVFP4_GEMM_LAUNCH(true, true); else NVFP4_GEMM_LAUNCH(true, false);
-  }
+#define NVFP4_GEMM_MODES(OB)                                     \
+  do {                                                           \
+    if (mode == kScalesLds) NVFP4_GEMM_LAUNCH(OB, kScalesLds);   \
+    else if (mode == kScalesU16) NVFP4_GEMM_LAUNCH(OB, kScalesU16); \
+    else NVFP4_GEMM_LAUNCH(OB, kScalesU8);                       \
+  } while (0)
+  if (c_dtype == 0) NVFP4_GEMM_MODES(false);
+  else NVFP4_GEMM_MODES(true);
+#undef NVFP4_GEMM_MODES
 #undef NVFP4_GEMM_LAUNCH
   return hipGetLastError();
 }
