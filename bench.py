@@ -41,8 +41,89 @@ def qbytes(n_elem: int, in_bytes: int) -> int:
     return n_elem * (2 * in_bytes) + n_elem // 2 + n_elem // 16
 
 
+def gemm_bytes(g) -> int:
+    """Algorithmic HBM bytes of one NVFP4 GEMM: both operands' codes (1/2 B)
+    and block scales (1/16 B) read once, the output written once."""
+    m, n, k = g.mnk
+    return (m + n) * k * 9 // 16 + m * n * (4 if g.out == "f32" else 2)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+# HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+# this script (FETCH_SIZE, then WRITE_SIZE), reduced by `--traffic` into the
+# JSON below.  Each counter is scaled by what it reads for a plain device copy
+# of known size that every run performs (CALIB_BYTES, outside the timed
+# region).  The profile records a hash of the kernel sources; when they have
+# changed since, the traffic is reported as null.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_f32_dgrad_wgrad_traffic.json")
+GEMM_SOURCES = [os.path.join(ROOT, "gemm_amax_reduce_amd", "csrc", f) for f in ("gemm.hip", "nvfp4_device.h")]
+DOMINANT = "k_gemm_nvfp4<false, 2>"      # f32 output, block scales staged in LDS
+CALIB_BYTES = 256 << 20
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """Measured HBM bytes per launch of the dominant kernel, or None."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if prof.get("source_sha256") != gemm_source_hash():
+        return None
+    return prof.get("bytes_per_launch")
+
+
+def reduce_traffic(fetch_dir: str, write_dir: str) -> dict:
+    """Average per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant
+    kernel and of the calibration copy from two rocprofv3 --pmc runs; the
+    copy's known size gives the scale factor of each counter."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        out = {}
+        for fn in files:
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = "dominant" if DOMINANT in name else "copy" if "copyBuffer" in name else None
+                if key:
+                    out.setdefault(key, []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    for name, got in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        if set(got) != {"dominant", "copy"}:
+            raise SystemExit(f"--traffic: {name} run lacks {sorted({'dominant', 'copy'} - set(got))} dispatches")
+    f_dom = sum(fetch["dominant"]) / len(fetch["dominant"])
+    w_dom = sum(write["dominant"]) / len(write["dominant"])
+    f_copy = max(fetch["copy"])      # the calibration copy is the largest copy
+    w_copy = max(write["copy"])
+    f_scale = CALIB_BYTES / (f_copy * 1024.0)
+    w_scale = CALIB_BYTES / (w_copy * 1024.0)
+    fetch_b = f_dom * 1024.0 * f_scale
+    write_b = w_dom * 1024.0 * w_scale
+    return {"kernel": DOMINANT, "source_sha256": gemm_source_hash(),
+            "fetch_kib_per_dispatch": f_dom, "write_kib_per_dispatch": w_dom,
+            "calibration_copy_bytes": CALIB_BYTES, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+            "bytes_per_launch": fetch_b + write_b, "dispatches": [len(fetch["dominant"]), len(write["dominant"])]}
 
 
 def main():
@@ -52,7 +133,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="reduce two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script into "
+                         "the traffic profile and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic:
+        prof = reduce_traffic(*args.traffic)
+        run = "--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-sweep"
+        prof["command"] = (f"rocprofv3 --pmc FETCH_SIZE -d {args.traffic[0]} -o run {run} && "
+                           f"rocprofv3 --pmc WRITE_SIZE -d {args.traffic[1]} -o run {run} && "
+                           f"python3 bench.py --traffic {args.traffic[0]} {args.traffic[1]}")
+        with open(TRAFFIC_PROFILE, "w") as f:
+            json.dump(prof, f, indent=1)
+        print(json.dumps(prof))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -81,6 +175,12 @@ def main():
     W2 = D.b.generate().to(dev)
     X2 = Wg.a.generate().to(dev)
     log(f"[bench] inputs generated and resident in HBM in {time.time() - t0:.1f}s")
+    # calibration copy of known size for the HBM traffic counters
+    calib_src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     # outputs preallocated: the timed loop allocates nothing
     qX1 = nv.NVFP4Tensor.empty(4096, 5120)
@@ -149,16 +249,20 @@ def main():
         else:
             breakdown[name] = {"ms": round(ms, 4), "TFLOP/s": round(kind[1] / (ms * 1e-3) / 1e12, 1)}
 
-    # dominant kernel: the f32-output GEMM (dgrad and wgrad launches, each
-    # 2*8192*5120*20480 flop); one nvfp4_gemm call is one kernel launch
+    # dominant kernel: the f32-output GEMM kernel (dgrad and wgrad launches,
+    # each 2*8192*5120*20480 flop); one nvfp4_gemm call is one kernel launch
+    # on torch's current stream, which the events above are recorded on
     gi = [i for i, (n, _, _) in enumerate(ops) if n in ("gemm dgrad", "gemm wgrad")]
     g_ms = float(np.mean(per_op[:, gi]))
     g_flop = D.flops
     achieved = g_flop / (g_ms * 1e-3) / 1e12
+    traffic = load_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None,
-                "kernel": "k_gemm_nvfp4<false> (f32 out), avg of dgrad+wgrad launches",
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                "traffic": round(traffic) if traffic else None,
+                "kernel": DOMINANT + " (f32 out), avg of the dgrad and wgrad launches",
                 "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flop,
+                "algorithmic_bytes_per_launch": int(np.mean([gemm_bytes(D), gemm_bytes(Wg)])),
                 "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4)}
 
     # ------------------------------------------------ quantizer sweep ----
@@ -220,8 +324,8 @@ def main():
 def cpu_baseline(F, D, Wg, mask, seed, step_flops):
     """The oracle (plain C + numpy float64) on a bounded sample of the step:
     all six quantizations in full, and for each GEMM the full oracle on a
-    slice of 64 output rows; the step time is extrapolated as
-    t(quantize) + sum_g t(slice_g) * M_g / 64."""
+    slice of 512 output rows; the step time is extrapolated as
+    t(quantize) + sum_g t(slice_g) * M_g / 512."""
     import numpy as np
 
     import oracle
@@ -229,7 +333,7 @@ def cpu_baseline(F, D, Wg, mask, seed, step_flops):
 
     t_q = 0.0
     t_g = 0.0
-    rows_sample = 64
+    rows_sample = 512
     for g in (F, D, Wg):
         refs = []
         for op in (g.a, g.b):
