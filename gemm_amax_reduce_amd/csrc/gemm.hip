@@ -16,32 +16,37 @@
 // is exact in f16, and every 16-element partial sum of the f16 MFMA is exact
 // in f32.
 //
-// Decode once per workgroup.  A 256-thread workgroup computes a 256 x BN
-// tile of C with four waves of 128 x BN/2 (4 x BN/64 v_mfma_f32_32x32x16_f16
-// tiles; BN = 256 gives 256 f32 accumulators per lane, held in AGPRs).  K
-// advances 64 elements per stage.  Each stage the workgroup loads the packed
-// codes (32 bytes per row) and block scales of its 256 A rows and BN B rows
-// with range-checked buffer loads, decodes them ONCE to f16 and writes them
-// to LDS in MFMA operand order: a 32x16 operand fragment is 1 KB, lane l's
-// 16 bytes at offset 16*l, so both the decoding writes and the MFMA operand
-// reads are contiguous 1 KB wave accesses with no bank conflicts.  Two LDS
-// stages are double-buffered (2 x 64 KB).  The decode of stage s+1 is
-// interleaved by hand with the MFMAs of stage s, and the global loads run PF
-// (= 2) stages ahead of the decode.  Decoding per workgroup instead of per
-// wave halves the conversion work (each operand row feeds two waves).
+// Data movement.  A 256-thread workgroup computes a 256 x BN tile of C (BN =
+// 256, or 128 for the column remainder) with four waves of 128 x BN/2.  K is
+// consumed in groups of 256 (four 64-wide stages).  For each group the
+// workgroup copies the packed codes of its 256 + BN operand rows -- one full
+// 128-byte line per row -- and their 16 scale bytes into LDS with the
+// buffer-load-to-LDS (DMA) form, double-buffered, so one load instruction
+// covers 8 rows with whole lines.  (Loading per lane in MFMA operand order,
+// lane l its own row, touches 32 lines per instruction; that line traffic
+// measured costlier than the whole decode.)  Each wave then reads only its
+// own operand rows from LDS (16 bytes = 32 codes per row and stage), decodes
+// them per K step into MFMA operand registers, and interleaves that decode
+// with the MFMAs of the previous K step.  Nothing decoded goes back to LDS,
+// so LDS carries about 100 KB per 4-stage group instead of 768 KB when
+// decoded operands are shared through it (LDS writes run at ~70 B/clk/CU).
 //
-// K order inside a fragment: lane l (row l%32, half h = l/32) holds the 8
-// consecutive K positions 16*ks + 8*h .. +7 of K step ks, for A and B alike,
-// which is the operand layout the MFMA sums over.
+// LDS image of a group: row R's 128 code bytes at R*128, its 16-byte chunk c
+// (32 K positions) in slot c ^ (R & 7), so the rows read by one ds_read_b128
+// fall on distinct banks; row R's 16 scale bytes at kCodeBytes + R*16.  A
+// rows are LDS rows 0..255, B rows 256.. .
+//
+// K order inside an MFMA operand: lane l (row l%32, half h = l/32) of stage
+// s' (0..3) of a group takes chunk 2s'+h, and K step ks its positions
+// 8ks..8ks+7 -- the same for A and B, which is all the MFMA's sum over K
+// requires.
 //
 // Grid: one workgroup per tile.  The launcher covers most columns with
 // 256 x 256 tiles and the remainder with 256 x 128 tiles in the same launch,
-// so the tile count fills whole rounds of the CUs (a single 256 x 320 tile
-// would need 320 accumulators per lane, more than the 256 AGPRs the
-// compiler keeps MFMA accumulators in).  Workgroups are dealt round-robin
-// to the eight XCDs (pid % 8); the tile index is remapped so each XCD works
-// on a contiguous range of tiles, ordered in groups of 8 tile rows, so that
-// the tiles resident on one XCD share A rows and B columns in its L2.
+// so the tile count fills whole rounds of the CUs.  Workgroups are dealt
+// round-robin to the eight XCDs (pid % 8); the tile index is remapped so each
+// XCD works on a contiguous range of tiles, ordered in groups of 8 tile rows,
+// so the tiles resident on one XCD share A rows and B columns in its L2.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -52,62 +57,27 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int BM = 256, BK = 64;
+constexpr int BM = 256;
 constexpr int kThreads = 256;
-constexpr int kFrag = 1024;                        // one 32x16 f16 operand fragment
-constexpr int kKSteps = BK / 16;                   // 4 MFMA K steps per stage
-constexpr int kGroupM = 8;                         // tile rows per L2 group
+constexpr int kGroupK = 256;                        // K positions per LDS group (4 stages)
+constexpr int kRowsMax = BM + 256;                  // operand rows of the widest tile
+constexpr int kCodeBytes = kRowsMax * 128;          // 64 KB of codes per group buffer
+constexpr int kGroupBytes = kCodeBytes + kRowsMax * 16;
+constexpr int kGroupM = 8;                          // tile rows per L2 group
 constexpr int kXcds = 8;
-constexpr int kCodeLoadPolicy = 1;                // buffer-load cache policy bits: sc0
-// Where the decode takes the block scales from: per stage and chunk, one
-// byte load each (any K), one 16-bit load (K % 32 == 0), or from 4-stage
-// scale groups staged in LDS (K % 64 == 0, 4-byte aligned scale arrays).
-constexpr int kScalesU8 = 0, kScalesU16 = 1, kScalesLds = 2;
-constexpr int kScaleGroupBytes = 2 * 256 * 16;      // one group: 512 tile rows x 16 bytes
-
-template <int BN>
-struct TileCfg {
-  static_assert(BN % 64 == 0, "wave tile width must be a multiple of 32");
-  static constexpr int kNB = BN / 64;                          // B fragments per wave
-  static constexpr int kGroups = (BM + BN) / 32;               // 32-row groups per stage
-  static constexpr int kSlots = (kGroups + 3) / 4;             // chunk slots per thread
-  static constexpr int kHalfA = (BM / 32) * kKSteps * kFrag;   // A part of a stage
-  static constexpr int kStage = kHalfA + (BN / 32) * kKSteps * kFrag;
-};
+constexpr uint32_t kOutOfRange = 0x80000000u;       // buffer offset past every view
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// Range-checked buffer view of one operand's tile rows: loads past the
-// view's size return zero, which pads the M and N edges.
-struct TileView {
-  __amdgpu_buffer_rsrc_t codes;
-  __amdgpu_buffer_rsrc_t scales;
-};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
   // 0x00020000: 32-bit data format word of a raw (stride 0) buffer on gfx9.
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Global-memory image of one thread's share of a stage: up to kSlots
-// 16-byte code chunks (32 K positions of one row each) and their two block
-// scales apiece.
-template <int NS>
-struct StageRegs {
-  u32x4 c[NS];
-  uint32_t s[NS];
-};
-
-// 8 codes (one word, element 0 in the low nibble) times the f16 pair of
-// block scales selected by `hi` -> 8 exact f16 values, as 4 words.
-__device__ __forceinline__ u32x4 decode8(uint32_t w, half2_t s2, bool hi) {
-  const half2_t s = hi ? (half2_t){s2[1], s2[1]} : (half2_t){s2[0], s2[0]};
-  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-  return (u32x4){__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+// 16 bytes per lane from a buffer view into LDS at dst + 16 * lane (the
+// gfx950 DMA form of buffer_load_dwordx4; dst must be wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t v, uint8_t *dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(v, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -117,28 +87,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // One 256 x BN output tile: workgroup `pid` of the tiles of C[M][N] = A.B^T
 // (B, C and N already restricted to this tile width's column range).
-template <bool OUT_BF16, int SCALES, int BN, int PF>
-__device__ __forceinline__ void gemm_tile(uint8_t *smem, uint8_t *sbuf, int pid, const uint8_t *__restrict__ A,
+template <bool OUT_BF16, bool SCALE_DMA, int BN>
+__device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t *__restrict__ A,
                                           const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
                                           const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
                                           const float *__restrict__ metaB, int64_t M, int64_t N, int64_t K,
                                           void *__restrict__ C, int64_t ldc) {
-  using Cfg = TileCfg<BN>;
-  constexpr int NB = Cfg::kNB, NS = Cfg::kSlots;
+  constexpr int NB = BN / 64;          // B fragments (32 columns each) per wave
+  constexpr int NF = 4 + NB;           // operand fragments decoded per wave and K step
+  constexpr int NU = 4 * NB;           // MFMAs per wave and K step
+  constexpr int kRowsB = BN / 2;       // B rows copied by each of waves 2 and 3
+  static_assert(BN == 256 || BN == 128, "tile width");
 
   // The wave index is uniform across a wave; readfirstlane tells the
-  // compiler so, which keeps every per-slot choice (A or B view, the
-  // last-slot test) in scalar registers.
+  // compiler so, which keeps every per-wave choice in scalar registers.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
 
   // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   const int xcd = pid % kXcds, local = pid / kXcds;
-  const int q = ntiles / kXcds, r = ntiles % kXcds;
-  const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int q = ntiles / kXcds, rq = ntiles % kXcds;
+  const int logical = (xcd < rq) ? xcd * (q + 1) + local : rq * (q + 1) + (xcd - rq) * q + local;
   const int per_group = kGroupM * tiles_n;
   const int group = logical / per_group;
   const int first_m = group * kGroupM;
@@ -147,130 +118,66 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, uint8_t *sbuf, int pid,
   const int tn = (logical % per_group) / gsz;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  // ---- operand views restricted to this tile's rows
-  const uint32_t row_bytes = (uint32_t)(K / 2), row_scales = (uint32_t)(K / 16);
-  const uint32_t rows_a = (uint32_t)(M - m0 < BM ? M - m0 : BM);
-  const uint32_t rows_b = (uint32_t)(N - n0 < BN ? N - n0 : BN);
-  const TileView va{make_rsrc(A + m0 * row_bytes, rows_a * row_bytes),
-                    make_rsrc(SA + m0 * row_scales, rows_a * row_scales)};
-  const TileView vb{make_rsrc(B + n0 * row_bytes, rows_b * row_bytes),
-                    make_rsrc(SB + n0 * row_scales, rows_b * row_scales)};
-
-  // ---- this thread's decode share.  Slot j of wave w is the 32-row group
-  // g = 4j + w of the stage (A rows for g < 8, B rows after), lane l takes
-  // row l%32 of the group and K half c = l/32 (32 positions) of the stage.
-  // The last slot exists only on the waves with g < kGroups.
-  const int c = lh;
-  const bool last_slot = 4 * (NS - 1) + wave < Cfg::kGroups;
-  // Slot j's row is base_row + 128*jj (jj = j for A slots, j - 2 for B
-  // slots): one lane offset per operand view plus a uniform (SGPR) offset.
-  const uint32_t base_row = 32 * wave + l32;
-  const uint32_t voff_code = base_row * row_bytes + 16 * c;
-  const uint32_t voff_scale = base_row * row_scales + 2 * c;
-  // fragment (rg, ks = 2c + wd/2), lane slot l32 + 32*(wd%2): slot j adds
-  // j * 16 KB (A and B parts are contiguous), word wd adds its own offset.
-  const uint32_t lds_base = (wave * kKSteps + 2 * c) * kFrag + l32 * 16;
-  auto is_b_slot = [&](int j) { return 4 * j + wave >= BM / 32; };
-  auto slot_rows = [&](int j) { return (uint32_t)(128 * (j < 2 ? j : j - 2)); };
-  static_assert(Cfg::kHalfA == 2 * 4 * kKSteps * kFrag, "B part must follow the two A slots");
-
-  // Global loads of one chunk of a stage into registers.  TAIL masks the K
-  // positions past K (the last, partial stage and any stage beyond it come
-  // out zero).
-  auto load_chunk = [&](StageRegs<NS> &st, int j, int64_t k0, auto tail) {
-    constexpr bool TAIL = decltype(tail)::value;
-    const uint32_t kb = (uint32_t)(k0 / 2), ksc = (uint32_t)(k0 / 16);
-    const bool b = is_b_slot(j);
-    const __amdgpu_buffer_rsrc_t rc = b ? vb.codes : va.codes, rs = b ? vb.scales : va.scales;
-    const uint32_t so_c = slot_rows(j) * row_bytes + kb, so_s = slot_rows(j) * row_scales + ksc;
-    // sc0 (workgroup-scope cache policy): a stage reads only 32 bytes of
-    // each row's 128-byte line and the 512 rows' lines do not stay in the
-    // 32 KB vector L1 until the next stage, so L1 allocation only multiplies
-    // the L2 -> L1 traffic; measured 12-20 % faster than the default policy.
-    st.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff_code, so_c, kCodeLoadPolicy));
-    if constexpr (SCALES == kScalesU16) {
-      st.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_scale, so_s, 0);
-    } else if constexpr (SCALES == kScalesU8) {  // a row's scales may start at an odd address
-      st.s[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, voff_scale, so_s, 0) |
-                ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, voff_scale, so_s + 1, 0) << 8);
-    }
-    if constexpr (TAIL) {
-      const int64_t kvalid = K - k0 - 32 * c;   // valid K positions of this thread's chunk
-      const uint32_t keep_lo = kvalid >= 16 ? ~0u : 0u, keep_hi = kvalid >= 32 ? ~0u : 0u;
-      st.c[j].x &= keep_lo;
-      st.c[j].y &= keep_lo;
-      st.c[j].z &= keep_hi;
-      st.c[j].w &= keep_hi;
-      if constexpr (SCALES != kScalesLds) st.s[j] &= (keep_lo & 0xFFu) | (keep_hi & 0xFF00u);
-    }
-  };
-  auto load_stage = [&](StageRegs<NS> &st, int64_t k0, auto tail) {
+  // ---- DMA side: waves 0 and 1 copy A rows 128w .. 128w+127, waves 2 and
+  // 3 B rows kRowsB(w-2) ..; a view holds only rows inside the operand, so
+  // rows past M or N read as zeros.
+  const uint32_t rb = (uint32_t)(K / 2), rs = (uint32_t)(K / 16);
+  const bool dma_b = wave >= 2;
+  const int64_t drow0 = dma_b ? n0 + (int64_t)kRowsB * (wave - 2) : m0 + 128 * (int64_t)wave;
+  const int64_t dlimit = dma_b ? N : M;
+  const int64_t dbase = min<int64_t>(drow0, dlimit);
+  const uint32_t dvalid = (uint32_t)min<int64_t>(dma_b ? kRowsB : 128, dlimit - dbase);
+  const __amdgpu_buffer_rsrc_t dcodes = make_rsrc((dma_b ? B : A) + dbase * rb, dvalid * rb);
+  const __amdgpu_buffer_rsrc_t dscales = make_rsrc((dma_b ? SB : SA) + dbase * rs, dvalid * rs);
+  const int lds_row0 = dma_b ? BM + kRowsB * (wave - 2) : 128 * wave;
+  // A 256 x 128 tile has 384 operand rows: its B waves copy 64 rows each and
+  // send the rest of their 16 + 2 instructions, out of range (no memory
+  // access), to the unused LDS rows 384..511, which keeps the instruction
+  // stream the same for every wave (no branch in the main loop).
+  const int spare_row0 = BM + 128 + 64 * (wave - 2);
+  // code DMA instruction: 8 rows, lane l -> row l>>3, LDS slot l&7, which
+  // holds the row's chunk (l&7) ^ (row&7)
+  const uint32_t dv_code = (uint32_t)(lane >> 3) * rb + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t dv_scale = (uint32_t)lane * rs;     // scale DMA: 64 rows, lane l -> row l
+  const int ng = (int)((K + kGroupK - 1) / kGroupK);
+  // Group g into LDS buffer buf.  A group past the last one gets offsets
+  // beyond every view: the range check then drops all lanes, so the DMA of
+  // the prefetch distance needs no branch at the end of K.
+  auto dma_group = [&](int g, int buf) {
+    uint8_t *gbuf = smem + buf * kGroupBytes;
+    const bool gin = g < ng;
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (j < NS - 1 || last_slot) load_chunk(st, j, k0, tail);
-  };
-
-  // The two E4M3 block scales of chunk j for stage t (the chunk's 32 K
-  // positions span two 16-blocks), as an f16 pair.  With SCALES ==
-  // kScalesLds they come from the workgroup's LDS scale groups: group gg
-  // holds stages 4gg .. 4gg+3, 16 bytes per tile row (A rows 0..255, B rows
-  // 256..), in buffer gg % 2.
-  auto chunk_scales = [&](const StageRegs<NS> &st, int j, int t) {
-    uint32_t sc;
-    if constexpr (SCALES == kScalesLds) {
-      const uint32_t row = (is_b_slot(j) ? BM : 0) + base_row + slot_rows(j);
-      sc = *reinterpret_cast<const uint16_t *>(sbuf + ((t >> 2) & 1) * kScaleGroupBytes + row * 16 + 4 * (t & 3) + 2 * c);
-    } else {
-      sc = st.s[j];
+    for (int qq = 0; qq < 16; ++qq) {
+      const bool real = !(BN == 128 && dma_b && qq >= 8);
+      const int lrow = real ? lds_row0 + 8 * qq : spare_row0 + 8 * (qq - 8);
+      dma16(dcodes, gbuf + lrow * 128, dv_code, (gin && real) ? 128u * (uint32_t)g + 8u * qq * rb : kOutOfRange);
     }
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
-  };
-  // Decode word wd (8 codes) of chunk j into the LDS stage buffer: word wd
-  // goes to K step 2c + wd/2, lane slot l32 + 32*(wd%2).
-  auto decode_word = [&](const StageRegs<NS> &st, int j, int wd, half2_t s2, uint8_t *buf) {
-    const uint32_t w = wd == 0 ? st.c[j].x : wd == 1 ? st.c[j].y : wd == 2 ? st.c[j].z : st.c[j].w;
-    uint8_t *dst = buf + lds_base + j * (4 * kKSteps * kFrag) + (wd >> 1) * kFrag + (wd & 1) * (32 * 16);
-    *reinterpret_cast<u32x4 *>(dst) = decode8(w, s2, wd >= 2);
-  };
-  auto store_stage = [&](const StageRegs<NS> &st, int t, uint8_t *buf) {
+    if constexpr (SCALE_DMA) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (j < NS - 1 || last_slot) {
-        const half2_t s2 = chunk_scales(st, j, t);
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) decode_word(st, j, wd, s2, buf);
+      for (int qq = 0; qq < 2; ++qq) {
+        const bool real = !(BN == 128 && dma_b && qq >= 1);
+        const int lrow = real ? lds_row0 + 64 * qq : spare_row0;
+        dma16(dscales, gbuf + kCodeBytes + lrow * 16, dv_scale,
+              (gin && real) ? 16u * (uint32_t)g + 64u * qq * rs : kOutOfRange);
       }
-  };
-
-  // Scale groups (SCALES == kScalesLds): thread tid loads 16 bytes (the
-  // scales of 4 stages) of A row tid and of B row tid -- one 16-byte load
-  // per row per 4 stages instead of a 2-byte load per chunk per stage -- and
-  // writes them to LDS two stages later.  Scales past K read as zero.
-  u32x4 sgr[2];
-  auto load_sgroup = [&](int gg) {
-    const uint32_t so = (uint32_t)(16 * gg);
-    sgr[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(va.scales, tid * row_scales, so, 0));
-    sgr[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vb.scales, tid * row_scales, so, 0));
-  };
-  // The K tail is masked here, when the loaded data is consumed, so the
-  // loads stay in flight for two stages.
-  auto store_sgroup = [&](int gg) {
-    const int64_t valid = (int64_t)row_scales - 16 * (int64_t)gg;   // valid bytes of this group
-    if (valid < 16) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int64_t nb = valid - 4 * q4;
-          const uint32_t keep = nb >= 4 ? ~0u : nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u);
-          sgr[h][q4] &= keep;
-        }
     }
-    uint8_t *dst = sbuf + (gg & 1) * kScaleGroupBytes;
-    *reinterpret_cast<u32x4 *>(dst + tid * 16) = sgr[0];
-    *reinterpret_cast<u32x4 *>(dst + (BM + tid) * 16) = sgr[1];
   };
 
+  // ---- read side: A fragment i is LDS row 128wm + 32i + r, B fragment j
+  // row BM + (BN/2)wn + 32j + r.
+  const uint32_t a_row = 128 * wm + r, b_row = BM + (BN / 2) * wn + r;
+  // Without scale DMA each lane loads its two scale bytes itself, from views
+  // of this wave's A rows and B rows (byte loads: the range check is exact).
+  __amdgpu_buffer_rsrc_t sview_a, sview_b;
+  if constexpr (!SCALE_DMA) {
+    const int64_t ar0 = min<int64_t>(m0 + 128 * wm, M), br0 = min<int64_t>(n0 + (BN / 2) * wn, N);
+    sview_a = make_rsrc(SA + ar0 * rs, (uint32_t)min<int64_t>(128, M - ar0) * rs);
+    sview_b = make_rsrc(SB + br0 * rs, (uint32_t)min<int64_t>(BN / 2, N - br0) * rs);
+  }
+  u32x4 codes[2][NF];      // [stage parity][fragment]: this lane's 32 codes
+  uint32_t sraw[NF];       // their two E4M3 block scales
+  half2_t spair[NF];       // ... as an f16 pair
+  half8_t opnd[2][NF];     // [K step parity][fragment]: decoded MFMA operands
   float16_t acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -279,144 +186,131 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, uint8_t *sbuf, int pid,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int a_frag0 = (4 * wm) * kKSteps * kFrag + lane * 16;
-  const int b_frag0 = Cfg::kHalfA + (NB * wn) * kKSteps * kFrag + lane * 16;
+  // Codes and scales of stage sp of group g (LDS buffer gb) into codes[cb].
+  // The scales of 16-blocks at or past K are zeroed, which zeroes those
+  // products whatever codes the DMA left there (every E2M1 value is finite).
+  const int k32 = (int)K;    // K < 2^25 (checked by the launcher)
+  auto read_stage = [&](int cb, const uint8_t *gb, int g, int sp) {
+    const int c = 2 * sp + h;
+    const uint32_t slot = (uint32_t)((c ^ (r & 7)) * 16);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint32_t row = f < 4 ? a_row + 32 * f : b_row + 32 * (f - 4);
+      codes[cb][f] = *reinterpret_cast<const u32x4 *>(gb + row * 128 + slot);
+      if constexpr (SCALE_DMA) {
+        sraw[f] = *reinterpret_cast<const uint16_t *>(gb + kCodeBytes + row * 16 + 2 * c);
+      } else {
+        const __amdgpu_buffer_rsrc_t v = f < 4 ? sview_a : sview_b;
+        const uint32_t vo = (uint32_t)r * rs + 2 * h;
+        const uint32_t so = 16u * (uint32_t)g + 4u * sp + 32u * (uint32_t)(f < 4 ? f : f - 4) * rs;
+        sraw[f] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(v, vo, so, 0) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(v, vo, so + 1, 0) << 8);
+      }
+    }
+    const int kc = kGroupK * g + 32 * c;
+    const uint32_t keep = (kc < k32 ? 0x00FFu : 0u) | (kc + 16 < k32 ? 0xFF00u : 0u);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) sraw[f] &= keep;
+  };
+  auto scale_pairs = [&]() {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) spair[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[f], 1.0f, false);
+  };
+  // Half `part` (bytes 2part, 2part+1 = 4 codes) of word ks of fragment f:
+  // K step ks lies in 16-block ks/2 of the chunk.
+  auto decode_half = [&](int cb, int ks, int f, int part, int db) {
+    const u32x4 cw = codes[cb][f];
+    const uint32_t w = ks == 0 ? cw.x : ks == 1 ? cw.y : ks == 2 ? cw.z : cw.w;
+    const half2_t p = spair[f];
+    const half2_t s = (ks >> 1) ? (half2_t){p[1], p[1]} : (half2_t){p[0], p[0]};
+    const half2_t x0 = (part ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * s;
+    const half2_t x1 = (part ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)) * s;
+    half8_t &d = opnd[db][f];
+    d[4 * part + 0] = x0[0];
+    d[4 * part + 1] = x0[1];
+    d[4 * part + 2] = x1[0];
+    d[4 * part + 3] = x1[1];
+  };
 
-  using Full = std::false_type;
-  using Tail = std::true_type;
-  const int nk = (int)((K + BK - 1) / BK);   // stages
-  const int nfull = (int)(K / BK);           // stages with all 64 K positions valid
-  // PF register sets: stage t lives in st[t % PF] from its load until it is
-  // decoded, PF stages later.
-  static_assert(PF == 1 || PF == 2, "prefetch depth");
-  StageRegs<NS> st[PF];
-  if constexpr (SCALES == kScalesLds) {
-    load_sgroup(0);
-    store_sgroup(0);
-    __syncthreads();
-  }
-  load_stage(st[0], 0, Tail{});
-  store_stage(st[0], 0, smem);
-  load_stage(st[1 % PF], BK, Tail{});
-  if constexpr (PF == 2) load_stage(st[0], 2 * BK, Tail{});
+  // ---- prologue: groups 0 and 1 in flight, stage 0 read, K step 0 decoded
+  dma_group(0, 0);
+  dma_group(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  read_stage(0, smem, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);     // nothing outstanding at loop entry
+  scale_pairs();
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    decode_half(0, 0, f, 0, 0);
+    decode_half(0, 0, f, 1, 0);
+  }
 
-  // One main-loop stage: the MFMAs of stage s read buffer `cur` while stage
-  // s+1 is decoded from `dec` into `nxt` and stage s+1+PF is loaded into
-  // `dec`.
-  // The instruction order is fixed by hand (sched_barrier fences): each
-  // group of NB MFMAs (NB x 32 cycles of the matrix core) is followed by one
-  // decode unit (one word: 4 conversions, 4 packed multiplies, one 16-byte
-  // LDS write), so the decode's VALU work runs while the MFMAs execute; the
-  // operand fragments of the next K step are read one step ahead; a chunk's
-  // global loads are issued as soon as its registers are decoded.
-  half8_t af[4], bf[2][NB];
-  auto read_a = [&](const uint8_t *cur, int ks, int i) {
-    af[i] = *reinterpret_cast<const half8_t *>(cur + a_frag0 + (i * kKSteps + ks) * kFrag);
-  };
-  auto read_b = [&](const uint8_t *cur, int ks, half8_t *bf_) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      bf_[j] = *reinterpret_cast<const half8_t *>(cur + b_frag0 + (j * kKSteps + ks) * kFrag);
-  };
-  // `phase` = s % 4 (compile time): with LDS scale groups, phase 0 loads
-  // group s/4 + 1 and phase 2 writes it to LDS (the barrier ending that
-  // stage publishes it before stage 4(s/4 + 1) is decoded, in phase 3).
-  auto main_stage = [&](int s, StageRegs<NS> &dec, auto phase) {
+  // Stage s = 4g + P.  K step ks: its NU MFMAs, each followed by its share
+  // of the decode of the next K step (of this stage, or K step 0 of the next
+  // stage), the order fixed by sched_barrier fences.  K step 1 reads the
+  // next stage's codes from LDS; in the last stage of a group it first waits
+  // for this wave's DMA of group g+1 and meets the other waves at the
+  // barrier -- after which group g+1 is in LDS and no wave reads group g any
+  // more -- reads stage 0 of group g+1 and then starts the DMA of group g+2
+  // into group g's buffer (after the reads, so that per-lane scale loads
+  // do not queue behind the DMA).
+  auto stage = [&](int g, auto phase) {
     constexpr int P = decltype(phase)::value;
-    const uint8_t *cur = smem + (s & 1) * Cfg::kStage;
-    uint8_t *nxt = smem + ((s & 1) ^ 1) * Cfg::kStage;
-    const int64_t kload = (int64_t)(s + 1 + PF) * BK;
-    half2_t s2[NS];
+    constexpr int cur = P & 1, nxt = cur ^ 1;
+    const uint8_t *gb = smem + (g & 1) * kGroupBytes;
+    const uint8_t *gn = smem + ((g + 1) & 1) * kGroupBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) read_a(cur, 0, i);
-    read_b(cur, 0, bf[0]);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      if (ks + 1 < kKSteps) read_b(cur, ks + 1, bf[(ks + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        // A fragment i of the next K step replaces the one just consumed.
-        if (ks + 1 < kKSteps) read_a(cur, ks + 1, i);
-        const int u = 4 * ks + i;       // decode unit: chunk u/4, word u%4
-        if ((u >> 2) < NS) {
-          if ((u & 3) == 0) s2[u >> 2] = chunk_scales(dec, u >> 2, s + 1);
-          decode_word(dec, u >> 2, u & 3, s2[u >> 2], nxt);
-          if ((u & 3) == 3) load_chunk(dec, u >> 2, kload, Full{});
+    for (int ks = 0; ks < 4; ++ks) {
+      const int dcur = ks & 1, dnxt = dcur ^ 1;
+      if (ks == 1) {
+        if (P == 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA of group g+1
+          __syncthreads();
+          read_stage(nxt, gn, g + 1, 0);
+          dma_group(g + 2, g & 1);
+        } else {
+          read_stage(nxt, gb, g, P + 1);
         }
-        if (NS > 4 && (u & 3) == 2 && last_slot) {   // the fifth chunk, one word per K step
-          if (ks == 0) s2[4] = chunk_scales(dec, 4, s + 1);
-          decode_word(dec, 4, ks, s2[4], nxt);
-          if (ks == 3) load_chunk(dec, 4, kload, Full{});
-        }
-        if constexpr (SCALES == kScalesLds) {
-          if (P == 0 && u == 1) load_sgroup(s / 4 + 1);
-          if (P == 2 && u == 9) store_sgroup(s / 4 + 1);
+      }
+      if (ks == 3) scale_pairs();
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc[u / NB][u % NB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(opnd[dcur][u / NB], opnd[dcur][4 + u % NB],
+                                                                     acc[u / NB][u % NB], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // decode halves [u*2NF/NU, (u+1)*2NF/NU) of the next K step
+#pragma unroll
+        for (int hv = (u * 2 * NF) / NU; hv < ((u + 1) * 2 * NF) / NU; ++hv) {
+          if (ks < 3)
+            decode_half(cur, ks + 1, hv >> 1, hv & 1, dnxt);
+          else
+            decode_half(nxt, 0, hv >> 1, hv & 1, dnxt);
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
   using P3 = std::integral_constant<int, 3>;
-
-  int s = 0;
-  if constexpr (SCALES == kScalesLds) {
-    static_assert(PF == 2, "the scale-group schedule assumes two register sets");
-    for (; s + PF + 4 < nfull; s += 4) {   // the code stages loaded here are all full
-      main_stage(s, st[1], P0{});
-      main_stage(s + 1, st[0], P1{});
-      main_stage(s + 2, st[1], P2{});
-      main_stage(s + 3, st[0], P3{});
-    }
-  } else {
-    for (; s + PF + 2 < nfull; s += 2) {   // the stages loaded here are all full
-      main_stage(s, st[1 % PF], P0{});
-      main_stage(s + 1, st[0], P1{});
-    }
+  for (int g = 0; g < ng; ++g) {
+    stage(g, P0{});
+    stage(g, P1{});
+    stage(g, P2{});
+    stage(g, P3{});
   }
-  // Tail: the last stages (loads may be partial or past K: zeros).
-  for (; s < nk; ++s) {
-    const uint8_t *cur = smem + (s & 1) * Cfg::kStage;
-    uint8_t *nxt = smem + ((s & 1) ^ 1) * Cfg::kStage;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) read_a(cur, ks, i);
-      read_b(cur, ks, bf[0]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[0][j], acc[i][j], 0, 0, 0);
-    }
-    if (PF == 2 && ((s + 1) & 1)) {
-      store_stage(st[1 % PF], s + 1, nxt);
-      load_stage(st[1 % PF], (int64_t)(s + 1 + PF) * BK, Tail{});
-    } else {
-      store_stage(st[0], s + 1, nxt);
-      load_stage(st[0], (int64_t)(s + 1 + PF) * BK, Tail{});
-    }
-    if constexpr (SCALES == kScalesLds) {   // same schedule as the main loop
-      if ((s & 3) == 0) load_sgroup(s / 4 + 1);
-      if ((s & 3) == 2) store_sgroup(s / 4 + 1);
-    }
-    __syncthreads();
-  }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- epilogue: C = (acc * gA) * gB.  Lane holds column l32 and rows
-  // 8*(e/4) + 4*lh + e%4 of each 32x32 tile; row offsets are uniform, so
-  // the per-store address is one lane base plus a scalar offset.
+  // ---- epilogue: C = (acc * gA) * gB.  Lane holds column r and rows
+  // 8*(e/4) + 4*h + e%4 of each 32x32 tile; row offsets are uniform, so the
+  // per-store address is one lane base plus a scalar offset.
   const float gA = metaA[1], gB = metaB[1];
-  const int64_t row_l = m0 + wm * 128 + 4 * lh, col_l = n0 + wn * (BN / 2) + l32;
+  const int64_t row_l = m0 + wm * 128 + 4 * h, col_l = n0 + wn * (BN / 2) + r;
   const bool full_tile = (m0 + BM <= M) && (n0 + BN <= N);
   using OutT = typename std::conditional<OUT_BF16, uint16_t, float>::type;
   OutT *base = reinterpret_cast<OutT *>(C) + row_l * ldc + col_l;
@@ -442,23 +336,21 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, uint8_t *sbuf, int pid,
 
 // The GEMM kernel: workgroups [0, n_big) compute the 256 x 256 tiles of
 // columns [0, n1), the others the 256 x 128 tiles of columns [n1, N).  The
-// branch is uniform per workgroup; LDS is sized for the larger tile (two
-// 64 KB decoded stages and two 8 KB scale groups).
-template <bool OUT_BF16, int SCALES>
+// branch is uniform per workgroup; LDS holds two group buffers sized for the
+// wider tile (2 x 72 KB).
+template <bool OUT_BF16, bool SCALE_DMA>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
              const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
              int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc, int n_big, int64_t n1) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TileCfg<256>::kStage + 2 * kScaleGroupBytes];
-  static_assert(TileCfg<128>::kStage <= TileCfg<256>::kStage, "LDS sized for the wide tile");
-  uint8_t *sbuf = smem + 2 * TileCfg<256>::kStage;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kGroupBytes];
   const int pid = blockIdx.x;
   if (pid < n_big) {
-    gemm_tile<OUT_BF16, SCALES, 256, 2>(smem, sbuf, pid, A, SA, metaA, B, SB, metaB, M, n1, K, C, ldc);
+    gemm_tile<OUT_BF16, SCALE_DMA, 256>(smem, pid, A, SA, metaA, B, SB, metaB, M, n1, K, C, ldc);
   } else {
     using OutT = typename std::conditional<OUT_BF16, uint16_t, float>::type;
-    gemm_tile<OUT_BF16, SCALES, 128, 2>(smem, sbuf, pid - n_big, A, SA, metaA, B + n1 * (K / 2), SB + n1 * (K / 16),
-                                        metaB, M, N - n1, K, reinterpret_cast<OutT *>(C) + n1, ldc);
+    gemm_tile<OUT_BF16, SCALE_DMA, 128>(smem, pid - n_big, A, SA, metaA, B + n1 * (K / 2), SB + n1 * (K / 16), metaB, M,
+                             N - n1, K, reinterpret_cast<OutT *>(C) + n1, ldc);
   }
 }
 
@@ -495,8 +387,9 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
     hipLaunchKernelGGL(k_zero_c, dim3(g), dim3(256), 0, stream, c, M, N, ldc, c_dtype == 0 ? 4 : 2);
     return hipGetLastError();
   }
-  // The buffer views address one tile's rows with 32-bit offsets.
-  if ((int64_t)BM * (K / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  // The DMA views address 128 rows with 32-bit offsets below the
+  // out-of-range marker 2^31 (this also keeps K below 2^25).
+  if ((int64_t)128 * (K / 2) >= (int64_t)kOutOfRange) return hipErrorInvalidValue;
   // Balance the grid over the CUs.  Columns [0, n1) get 256 x 256 tiles and
   // the rest 256 x 128 tiles (half the work per tile; their per-flop cost is
   // taken as 1.1x); n1 minimises the modelled time
@@ -518,23 +411,22 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
   const int64_t n_big = tm * (best_n1 / 256), n_small = tm * ((N - best_n1 + 127) / 128);
   if (n_big + n_small > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(n_big + n_small));
-  // Scale path: 16-byte scale-group loads need K % 64 == 0 (a row's scales
-  // then start on a 4-byte boundary) and 4-byte aligned scale arrays; 16-bit
-  // per-stage loads need K % 32 == 0; otherwise single bytes.
-  const bool a4 = ((uintptr_t)a_scales % 4 == 0) && ((uintptr_t)b_scales % 4 == 0);
-  const int mode = (K % 64 == 0 && a4) ? kScalesLds : (K % 32 == 0 ? kScalesU16 : kScalesU8);
-#define NVFP4_GEMM_LAUNCH(OB, SM)                                                                          \
-  hipLaunchKernelGGL((k_gemm_nvfp4<OB, SM>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, \
+  // Scale rows go through the DMA only when they are whole dwords (K % 64
+  // == 0): the range check of a view works per dword, and with a row pitch
+  // of K/16 bytes not a multiple of 4 the dword holding a view's last scale
+  // bytes reaches past the view and would be dropped whole.  Code rows
+  // (K/2 bytes) are always a multiple of 8.
+  const bool scale_dma = K % 64 == 0;
+#define NVFP4_GEMM_LAUNCH(OB, SD)                                                                          \
+  hipLaunchKernelGGL((k_gemm_nvfp4<OB, SD>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, \
                      b_codes, b_scales, b_meta, M, N, K, c, ldc, (int)n_big, best_n1)
-#define NVFP4_GEMM_MODES(OB)                                     \
-  do {                                                           \
-    if (mode == kScalesLds) NVFP4_GEMM_LAUNCH(OB, kScalesLds);   \
-    else if (mode == kScalesU16) NVFP4_GEMM_LAUNCH(OB, kScalesU16); \
-    else NVFP4_GEMM_LAUNCH(OB, kScalesU8);                       \
-  } while (0)
-  if (c_dtype == 0) NVFP4_GEMM_MODES(false);
-  else NVFP4_GEMM_MODES(true);
-#undef NVFP4_GEMM_MODES
+  if (c_dtype == 0) {
+    if (scale_dma) NVFP4_GEMM_LAUNCH(false, true);
+    else NVFP4_GEMM_LAUNCH(false, false);
+  } else {
+    if (scale_dma) NVFP4_GEMM_LAUNCH(true, true);
+    else NVFP4_GEMM_LAUNCH(true, false);
+  }
 #undef NVFP4_GEMM_LAUNCH
   return hipGetLastError();
 }
