@@ -140,19 +140,23 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   const uint32_t dv_code = (uint32_t)(lane >> 3) * rb + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
   const uint32_t dv_scale = (uint32_t)lane * rs;     // scale DMA: 64 rows, lane l -> row l
   const int ng = (int)((K + kGroupK - 1) / kGroupK);
-  // Group g into LDS buffer buf.  A group past the last one gets offsets
-  // beyond every view: the range check then drops all lanes, so the DMA of
-  // the prefetch distance needs no branch at the end of K.
-  auto dma_group = [&](int g, int buf) {
+  // Part `part` of the DMA of group g into LDS buffer buf.  The 16 code and
+  // 2 scale instructions of a group are spread over four stages (parts 3,
+  // 0, 1, 2 in issue order: code instructions 0-4, 5-9, 10-14, then 15 and
+  // the scales) instead of one burst.  A group past the last one gets
+  // offsets beyond every view: the range check then drops all lanes, so the
+  // DMA of the prefetch distance needs no branch at the end of K.
+  auto dma_part = [&](int g, int buf, int part) {
     uint8_t *gbuf = smem + buf * kGroupBytes;
     const bool gin = g < ng;
+    const int q0 = part == 3 ? 0 : 5 * part + 5, q1 = part == 3 ? 5 : part == 2 ? 16 : q0 + 5;
 #pragma unroll
-    for (int qq = 0; qq < 16; ++qq) {
+    for (int qq = q0; qq < q1; ++qq) {
       const bool real = !(BN == 128 && dma_b && qq >= 8);
       const int lrow = real ? lds_row0 + 8 * qq : spare_row0 + 8 * (qq - 8);
       dma16(dcodes, gbuf + lrow * 128, dv_code, (gin && real) ? 128u * (uint32_t)g + 8u * qq * rb : kOutOfRange);
     }
-    if constexpr (SCALE_DMA) {
+    if (SCALE_DMA && part == 2) {
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const bool real = !(BN == 128 && dma_b && qq >= 1);
@@ -234,9 +238,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
     d[4 * part + 3] = x1[1];
   };
 
-  // ---- prologue: groups 0 and 1 in flight, stage 0 read, K step 0 decoded
-  dma_group(0, 0);
-  dma_group(1, 1);
+  // ---- prologue: group 0 and the first part of group 1 in flight (the
+  // rest of group 1 follows in stages 0-2), stage 0 read, K step 0 decoded
+#pragma unroll
+  for (int part = 0; part < 4; ++part) dma_part(0, 0, part);
+  dma_part(1, 1, 3);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   read_stage(0, smem, 0, 0);
@@ -251,12 +257,13 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   // Stage s = 4g + P.  K step ks: its NU MFMAs, each followed by its share
   // of the decode of the next K step (of this stage, or K step 0 of the next
   // stage), the order fixed by sched_barrier fences.  K step 1 reads the
-  // next stage's codes from LDS; in the last stage of a group it first waits
-  // for this wave's DMA of group g+1 and meets the other waves at the
-  // barrier -- after which group g+1 is in LDS and no wave reads group g any
-  // more -- reads stage 0 of group g+1 and then starts the DMA of group g+2
-  // into group g's buffer (after the reads, so that per-lane scale loads
-  // do not queue behind the DMA).
+  // next stage's codes from LDS and then issues one part of the DMA of
+  // group g+1 (stages 0-2).  In the last stage of a group it first waits for
+  // this wave's DMA of group g+1 and meets the other waves at the barrier --
+  // after which group g+1 is in LDS and no wave reads group g any more --
+  // reads stage 0 of group g+1 and starts the DMA of group g+2 into group
+  // g's buffer.  The reads come before the DMA so that per-lane scale loads
+  // do not queue behind it.
   auto stage = [&](int g, auto phase) {
     constexpr int P = decltype(phase)::value;
     constexpr int cur = P & 1, nxt = cur ^ 1;
@@ -271,9 +278,10 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
           __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA of group g+1
           __syncthreads();
           read_stage(nxt, gn, g + 1, 0);
-          dma_group(g + 2, g & 1);
+          dma_part(g + 2, g & 1, 3);
         } else {
           read_stage(nxt, gb, g, P + 1);
+          dma_part(g + 1, (g + 1) & 1, P);
         }
       }
       if (ks == 3) scale_pairs();
