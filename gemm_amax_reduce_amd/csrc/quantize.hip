@@ -133,10 +133,12 @@ __global__ void __launch_bounds__(kQT) k_amax_rht_rows(const T *x, int64_t nchun
 //
 // K runs down the columns.  A thread owns kCPT adjacent columns (two bf16
 // columns share one 4-byte load, f32 takes one) and kNBT consecutive
-// 16-row blocks, so a wave reads 256 contiguous bytes of each row and a
-// workgroup 1 KB, and each output row (= input column) receives kNBT code
-// words (32 bytes) and kNBT scale bytes from one thread.  Grid: x over
-// column groups of 256 * kCPT, y over groups of kNBT blocks.
+// 16-row blocks, so a wave reads 256 contiguous bytes of each row, and each
+// output row (= input column) receives kNBT code words (32 bytes) and kNBT
+// scale bytes from one thread.  The encode's four waves share their columns
+// and take consecutive block groups (one 128-byte output line per column);
+// the amax pass of the RHT path uses 256 * kCPT columns x kNBT blocks per
+// workgroup.
 constexpr int kNBT = 4;
 
 template <typename T>
@@ -231,9 +233,16 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
   const float amax = meta[0];
   const TensorScales ts = tensor_scales(amax);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) meta[1] = ts.g;
-  const int64_t c = ((int64_t)(gridDim.x - 1 - blockIdx.x) * kQT + threadIdx.x) * CPT;
-  const int64_t nkb = rows / 16, kb0 = (int64_t)(gridDim.y - 1 - blockIdx.y) * kNBT;
-  if (c >= cols) return;
+  // The four waves of a workgroup take the same 64 * CPT columns and four
+  // consecutive groups of kNBT blocks, so they write the four 32-byte pieces
+  // of each 128-byte output line together: the line is complete in L2
+  // before it is written back (pieces from different workgroups, possibly on
+  // different XCDs, left L2 as partial lines: +25-45 % HBM write bytes).
+  static_assert(kQT == 256, "four waves per workgroup");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c = ((int64_t)(gridDim.x - 1 - blockIdx.x) * 64 + lane) * CPT;
+  const int64_t nkb = rows / 16, kb0 = ((int64_t)(gridDim.y - 1 - blockIdx.y) * 4 + wave) * kNBT;
+  if (c >= cols || kb0 >= nkb) return;
   const bool fast = (c + CPT <= cols) && (CPT == 1 || (cols % 2) == 0);
   const int nb = (int)(nkb - kb0 < kNBT ? nkb - kb0 : kNBT);
   uint2 cw[CPT][kNBT];
@@ -363,7 +372,8 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
   const int64_t nblocks = n / 16;
   unsigned g = grid_for(nblocks);
 #define NVFP4_QROWS(T, S, R) hipLaunchKernelGGL((k_quant_rows<T, S, R>), dim3(g), dim3(kQT), 0, stream, (const T *)x, nblocks, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
-#define NVFP4_QCOLS(T, S, R) hipLaunchKernelGGL((k_quant_cols<T, S, R>), tiles, dim3(kQT), 0, stream, (const T *)x, rows, cols, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
+  const dim3 qtiles((unsigned)((cols + 64 * cpt - 1) / (64 * cpt)), (unsigned)((rows / 16 + 4 * kNBT - 1) / (4 * kNBT)));
+#define NVFP4_QCOLS(T, S, R) hipLaunchKernelGGL((k_quant_cols<T, S, R>), qtiles, dim3(kQT), 0, stream, (const T *)x, rows, cols, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
 #define NVFP4_DISPATCH(MAC, T)                  \
   do {                                          \
     if (sr) { if (rht) MAC(T, true, true); else MAC(T, true, false); } \
