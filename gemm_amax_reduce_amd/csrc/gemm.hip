@@ -256,7 +256,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
 
   // Stage s = 4g + P.  K step ks: its NU MFMAs, each followed by its share
   // of the decode of the next K step (of this stage, or K step 0 of the next
-  // stage), the order fixed by sched_barrier fences.  K step 1 reads the
+  // stage), the order fixed by sched_barrier fences.  K step 0 reads the
   // next stage's codes from LDS and then issues one part of the DMA of
   // group g+1 (stages 0-2).  In the last stage of a group it first waits for
   // this wave's DMA of group g+1 and meets the other waves at the barrier --
@@ -272,7 +272,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int dcur = ks & 1, dnxt = dcur ^ 1;
-      if (ks == 1) {
+      if (ks == 0) {
         if (P == 3) {
           __builtin_amdgcn_sched_barrier(0);
           __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA of group g+1
@@ -288,8 +288,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         __builtin_amdgcn_sched_barrier(0);
-        acc[u / NB][u % NB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(opnd[dcur][u / NB], opnd[dcur][4 + u % NB],
-                                                                     acc[u / NB][u % NB], 0, 0, 0);
+        // snake order: the B fragment stays the same across the step to
+        // the next A fragment (MFMA power, hence clock, follows operand
+        // toggling)
+        const int mi = u / NB, mj = (mi & 1) ? NB - 1 - u % NB : u % NB;
+        acc[mi][mj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(opnd[dcur][mi], opnd[dcur][4 + mj], acc[mi][mj], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         // decode halves [u*2NF/NU, (u+1)*2NF/NU) of the next K step
 #pragma unroll
