@@ -9,6 +9,7 @@ resident in HBM before timing starts:
                        W [20480x5120] (RNE, axis 0), GEMM -> f32 [8192x5120]
   wgrad  dW = X^T dY : RHT-quantize X [8192x5120] (RNE, axis 0) and
                        dY [8192x20480] (SR, axis 0), GEMM -> f32 [5120x20480]
+dY's two quantizations run as one dual-layout call (one amax read for both).
 value = GEMM FLOP of the step / step time (quantization included), TFLOP/s.
 Also reported: quantizer GB/s per operand and on the 32768x8192 sweep tensor
 (RNE/SR x RHT off/on), per-GEMM TFLOP/s, the roofline of the dominant kernel
@@ -39,6 +40,13 @@ def qbytes(n_elem: int, in_bytes: int) -> int:
     """Algorithmic HBM bytes of one quantization: the input is read twice
     (amax pass, encode pass), codes (0.5 B) and scales (1/16 B) written."""
     return n_elem * (2 * in_bytes) + n_elem // 2 + n_elem // 16
+
+
+def qbytes_dual(n_elem: int, in_bytes: int) -> int:
+    """Algorithmic HBM bytes of a dual-layout quantization: the input is read
+    three times (one amax pass, two encode passes), two sets of codes and
+    scales written."""
+    return n_elem * (3 * in_bytes) + 2 * (n_elem // 2 + n_elem // 16)
 
 
 def gemm_bytes(g) -> int:
@@ -197,12 +205,14 @@ def main():
         ("q fprop X", lambda: nv.nvfp4_quantize(X1, axis=1, out=qX1), ("q", X1)),
         ("q fprop W", lambda: nv.nvfp4_quantize(W1, axis=1, out=qW1), ("q", W1)),
         ("gemm fprop", lambda: nv.nvfp4_gemm(qX1, qW1, torch.bfloat16, out=Y), ("g", F.flops)),
-        ("q dgrad dY (SR)", lambda: nv.nvfp4_quantize(dY, axis=1, rounding="sr", seed=seed, offset=0, out=qdY), ("q", dY)),
+        # dY in both layouts from one amax read: axis 1 SR (dgrad, offset 0)
+        # and axis 0 RHT SR (wgrad, offset 1)
+        ("q dY dual (axis1 SR + axis0 RHT SR)",
+         lambda: nv.nvfp4_quantize_dual(dY, rounding1="sr", seed1=seed, offset1=0, rht0=True, sign_mask0=mask,
+                                        rounding0="sr", seed0=seed, offset0=1, out1=qdY, out0=qdYt), ("q2", dY)),
         ("q dgrad W (axis0)", lambda: nv.nvfp4_quantize(W2, axis=0, out=qW2), ("q", W2)),
         ("gemm dgrad", lambda: nv.nvfp4_gemm(qdY, qW2, torch.float32, out=dX), ("g", D.flops)),
         ("q wgrad X (RHT, axis0)", lambda: nv.nvfp4_rht_quantize(X2, mask, axis=0, out=qX2), ("q", X2)),
-        ("q wgrad dY (RHT, SR, axis0)", lambda: nv.nvfp4_rht_quantize(dY, mask, axis=0, rounding="sr", seed=seed,
-                                                                      offset=1, out=qdYt), ("q", dY)),
         ("gemm wgrad", lambda: nv.nvfp4_gemm(qX2, qdYt, torch.float32, out=dW), ("g", Wg.flops)),
     ]
     step_flops = F.flops + D.flops + Wg.flops
@@ -242,9 +252,9 @@ def main():
     breakdown = {}
     for i, (name, _, kind) in enumerate(ops):
         ms = float(np.mean(per_op[:, i]))
-        if kind[0] == "q":
+        if kind[0] in ("q", "q2"):
             x = kind[1]
-            b = qbytes(x.numel(), x.element_size())
+            b = qbytes(x.numel(), x.element_size()) if kind[0] == "q" else qbytes_dual(x.numel(), x.element_size())
             breakdown[name] = {"ms": round(ms, 4), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)}
         else:
             breakdown[name] = {"ms": round(ms, 4), "TFLOP/s": round(kind[1] / (ms * 1e-3) / 1e12, 1)}

@@ -15,7 +15,7 @@ import os
 
 import torch
 
-__all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize",
+__all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual",
            "nvfp4_dequantize", "nvfp4_gemm", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +37,7 @@ class _CTensor(ctypes.Structure):
 _lib = None
 
 # every symbol the header declares
-EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_dequantize", "nvfp4_gemm",
+EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_dequantize", "nvfp4_gemm",
            "nvfp4_status_string")
 
 
@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize.restype = ci
         L.nvfp4_rht_quantize.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, ctypes.c_uint16, pt, vp]
         L.nvfp4_rht_quantize.restype = ci
+        L.nvfp4_quantize_dual.argtypes = [vp, ci, i64, i64, ci, u64, u64, pt, ci, ctypes.c_uint16, ci, u64, u64,
+                                          pt, vp]
+        L.nvfp4_quantize_dual.restype = ci
         L.nvfp4_dequantize.argtypes = [pt, vp, ci, vp]
         L.nvfp4_dequantize.restype = ci
         L.nvfp4_gemm.argtypes = [pt, pt, vp, ci, i64, vp]
@@ -149,6 +152,29 @@ def nvfp4_rht_quantize(x: torch.Tensor, sign_mask: int, axis: int = 1, rounding=
                        offset: int = 0, out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
     """Quantize after the 16-point random Hadamard transform along k."""
     return _quantize(x, axis, rounding, seed, offset, True, sign_mask, out, stream)
+
+
+def nvfp4_quantize_dual(x: torch.Tensor, rounding1="rne", seed1: int = 0, offset1: int = 0,
+                        rht0: bool = False, sign_mask0: int = 0, rounding0="rne", seed0: int = 0,
+                        offset0: int = 0, out1: NVFP4Tensor | None = None, out0: NVFP4Tensor | None = None,
+                        stream=None) -> tuple[NVFP4Tensor, NVFP4Tensor]:
+    """Both layouts of x with one amax read: (axis-1 tensor, axis-0 tensor),
+    bit-identical to the two single quantizations (see include/nvfp4.h)."""
+    _require_device(x, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise NVFP4Error("x must be a contiguous 2-D tensor")
+    rows, cols = x.shape
+    if out1 is None:
+        out1 = NVFP4Tensor.empty(rows, cols, device=x.device)
+    if out0 is None:
+        out0 = NVFP4Tensor.empty(cols, rows, device=x.device)
+    c1, c0 = out1._c(), out0._c()
+    rc = lib().nvfp4_quantize_dual(x.data_ptr(), _dtype_code(x), rows, cols, _rounding_code(rounding1), seed1,
+                                   offset1, ctypes.byref(c1), int(bool(rht0)), sign_mask0 & 0xFFFF,
+                                   _rounding_code(rounding0), seed0, offset0, ctypes.byref(c0),
+                                   _stream_handle(stream))
+    _check(rc, "nvfp4_quantize_dual")
+    return out1, out0
 
 
 def nvfp4_dequantize(q: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None,

@@ -53,6 +53,29 @@ int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, i
   return quantize_common(x, x_dtype, rows, cols, axis, rounding, seed, offset, true, sign_mask, out, hip_stream);
 }
 
+int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int rounding1, uint64_t seed1,
+                        uint64_t offset1, nvfp4_tensor *out1, int rht0, uint16_t sign_mask0, int rounding0,
+                        uint64_t seed0, uint64_t offset0, nvfp4_tensor *out0, void *hip_stream) {
+  if (!out1 || !out0) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if ((rounding1 != NVFP4_RNE && rounding1 != NVFP4_SR) || (rounding0 != NVFP4_RNE && rounding0 != NVFP4_SR))
+    return NVFP4_ERR_ENUM;
+  if (rht0 != 0 && rht0 != 1) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (out1->outer != rows || out1->k != cols || out0->outer != cols || out0->k != rows) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
+  int st = check_tensor(out1);
+  if (st != NVFP4_OK) return st;
+  st = check_tensor(out0);
+  if (st != NVFP4_OK) return st;
+  if (out1->meta == out0->meta) return NVFP4_ERR_SHAPE;   // the two maxima need their own words
+  if (!aligned(x, 16)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_quantize_dual(x, x_dtype, rows, cols, rounding1, seed1, offset1, out1->codes,
+                                                out1->scales, out1->meta, rht0 != 0, sign_mask0, rounding0, seed0,
+                                                offset0, out0->codes, out0->scales, out0->meta,
+                                                (hipStream_t)hip_stream));
+}
+
 int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stream) {
   int st = check_tensor(q);
   if (st != NVFP4_OK) return st;

@@ -15,6 +15,14 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
                            uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
                            uint8_t *scales, float *meta, hipStream_t stream);
 
+// One input, two quantizations with one amax read: the axis-1 output (no
+// transform) and the axis-0 output (with or without the RHT); each output is
+// bit-identical to launch_quantize's.
+hipError_t launch_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int rounding1,
+                                uint64_t seed1, uint64_t offset1, uint8_t *codes1, uint8_t *scales1, float *meta1,
+                                bool rht0, uint32_t sign_mask0, int rounding0, uint64_t seed0, uint64_t offset0,
+                                uint8_t *codes0, uint8_t *scales0, float *meta0, hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *meta, int64_t outer,
                              int64_t k, void *y, int y_dtype, hipStream_t stream);
 

@@ -61,10 +61,41 @@ __device__ __forceinline__ void block_max_atomic(uint32_t v, uint32_t *dst) {
   }
 }
 
+// block_max_atomic for two maxima at once (one LDS round).
+__device__ __forceinline__ void block_max2_atomic(uint32_t v0, uint32_t *dst0, uint32_t v1, uint32_t *dst1) {
+  __shared__ uint32_t part2[2][kQT / 64];
+  v0 = wave_max(v0);
+  v1 = wave_max(v1);
+  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    part2[0][wave] = v0;
+    part2[1][wave] = v1;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int t = threadIdx.x;
+    uint32_t m = part2[t][0];
+#pragma unroll
+    for (int i = 1; i < kQT / 64; ++i) m = max(m, part2[t][i]);
+    uint32_t *dst = t ? dst1 : dst0;
+    const uint32_t cur = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m > cur) atomicMax(dst, m);
+  }
+}
+
 __global__ void k_meta_init(float *meta) {
   if (threadIdx.x == 0) {
     meta[0] = 0.0f;
     meta[1] = 0.0f;
+  }
+}
+
+__global__ void k_meta_init2(float *meta_a, float *meta_b) {
+  if (threadIdx.x == 0) {
+    meta_a[0] = 0.0f;
+    meta_a[1] = 0.0f;
+    meta_b[0] = 0.0f;
+    meta_b[1] = 0.0f;
   }
 }
 
@@ -90,7 +121,8 @@ template <> __device__ __forceinline__ uint32_t vec_absmax<float>(uint4 v) {
 // read ~15 % faster than a grid-wide stride, which spreads every wave's
 // accesses over the whole tensor).
 template <typename T>
-__global__ void __launch_bounds__(kQT) k_amax_flat(const uint4 *x, int64_t n16, int64_t per_wg, uint32_t *amax_bits) {
+__global__ void __launch_bounds__(kQT) k_amax_flat(const uint4 *x, int64_t n16, int64_t per_wg, uint32_t *amax_bits,
+                                                  uint32_t *amax_bits2) {
   uint32_t m = 0;
   const int64_t beg = (int64_t)blockIdx.x * per_wg;
   const int64_t end = beg + per_wg < n16 ? beg + per_wg : n16;
@@ -100,7 +132,10 @@ __global__ void __launch_bounds__(kQT) k_amax_flat(const uint4 *x, int64_t n16, 
     m = max(max(m, vec_absmax<T>(v0)), max(vec_absmax<T>(v1), max(vec_absmax<T>(v2), vec_absmax<T>(v3))));
   }
   for (; i < end; i += kQT) m = max(m, vec_absmax<T>(x[i]));
-  block_max_atomic(m, amax_bits);
+  if (amax_bits2)   // the same maximum for a second tensor (dual-layout quantize)
+    block_max2_atomic(m, amax_bits, m, amax_bits2);
+  else
+    block_max_atomic(m, amax_bits);
 }
 
 // amax of the transformed tensor, axis 1: 16-chunks of rows, one contiguous
@@ -197,6 +232,34 @@ __global__ void __launch_bounds__(kQT) k_amax_rht_cols(const T *x, int64_t rows,
     }
   }
   block_max_atomic(m, amax_bits);
+}
+
+// Dual-layout amax: one read of x gives the plain maximum (for the axis-1
+// output) and the maximum after the column transform (for the axis-0 RHT
+// output).
+template <typename T>
+__global__ void __launch_bounds__(kQT) k_amax_dual_cols(const T *x, int64_t rows, int64_t cols, uint32_t sign_mask,
+                                                       uint32_t *plain_bits, uint32_t *rht_bits) {
+  constexpr int CPT = ColPairs<T>::kCPT;
+  const int64_t c = ((int64_t)blockIdx.x * kQT + threadIdx.x) * CPT;
+  const int64_t nkb = rows / 16, kb0 = (int64_t)blockIdx.y * kNBT;
+  const bool fast = (c + CPT <= cols) && (CPT == 1 || (cols % 2) == 0);
+  uint32_t mp = 0, mr = 0;
+  if (c < cols) {
+#pragma unroll
+    for (int i = 0; i < kNBT; ++i) {
+      if (kb0 + i >= nkb) break;
+      float y[CPT][16];
+      load_col_block<T>(x, cols, kb0 + i, c, fast, y);
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        mp = max(mp, absmax_bits16(y[e]));
+        rht16(y[e], sign_mask);
+        mr = max(mr, absmax_bits16(y[e]));
+      }
+    }
+  }
+  block_max2_atomic(mp, plain_bits, mr, rht_bits);
 }
 
 // ------------------------------------------------------------- encode ----
@@ -339,40 +402,19 @@ inline unsigned grid_for(int64_t work, int64_t per_block = kQT, int64_t cap = 1 
 
 }  // namespace
 
-hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
-                           uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
-                           uint8_t *scales, float *meta, hipStream_t stream) {
+namespace {
+
+// Pass 2 of a quantization (encode), reading amax from meta[0].
+void launch_encode(const void *x, bool bf16, int64_t rows, int64_t cols, int axis, int rounding, uint64_t seed,
+                   uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes, uint8_t *scales, float *meta,
+                   hipStream_t stream) {
   const int64_t n = rows * cols;
-  uint32_t *amax_bits = reinterpret_cast<uint32_t *>(meta);
-  hipLaunchKernelGGL(k_meta_init, dim3(1), dim3(64), 0, stream, meta);
-  if (n == 0) return hipGetLastError();
-  const bool bf16 = (x_dtype == 1);
   const int64_t cpt = bf16 ? 2 : 1;
-  const dim3 tiles((unsigned)((cols + kQT * cpt - 1) / (kQT * cpt)), (unsigned)((rows / 16 + kNBT - 1) / kNBT));
-  if (axis == 0 && (rows / 16 + kNBT - 1) / kNBT > 65535) return hipErrorInvalidValue;
-  // pass 1: amax
-  if (!rht) {
-    const int64_t n16 = n * (bf16 ? 2 : 4) / 16;
-    const unsigned g = grid_for(n16, kQT * 4, 1024);
-    const int64_t per = (n16 + g - 1) / g;
-    if (bf16) hipLaunchKernelGGL(k_amax_flat<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits);
-    else hipLaunchKernelGGL(k_amax_flat<float>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits);
-  } else if (axis == 1) {
-    const int64_t nch = n / 16;
-    const unsigned g = grid_for(nch, kQT * 2, 2048);
-    const int64_t per = (nch + g - 1) / g;
-    if (bf16) hipLaunchKernelGGL(k_amax_rht_rows<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint16_t *)x, nch, per, sign_mask, amax_bits);
-    else hipLaunchKernelGGL(k_amax_rht_rows<float>, dim3(g), dim3(kQT), 0, stream, (const float *)x, nch, per, sign_mask, amax_bits);
-  } else {
-    if (bf16) hipLaunchKernelGGL(k_amax_rht_cols<uint16_t>, tiles, dim3(kQT), 0, stream, (const uint16_t *)x, rows, cols, sign_mask, amax_bits);
-    else hipLaunchKernelGGL(k_amax_rht_cols<float>, tiles, dim3(kQT), 0, stream, (const float *)x, rows, cols, sign_mask, amax_bits);
-  }
-  // pass 2: encode
   const bool sr = (rounding == 1);
   const int64_t nblocks = n / 16;
   unsigned g = grid_for(nblocks);
-#define NVFP4_QROWS(T, S, R) hipLaunchKernelGGL((k_quant_rows<T, S, R>), dim3(g), dim3(kQT), 0, stream, (const T *)x, nblocks, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
   const dim3 qtiles((unsigned)((cols + 64 * cpt - 1) / (64 * cpt)), (unsigned)((rows / 16 + 4 * kNBT - 1) / (4 * kNBT)));
+#define NVFP4_QROWS(T, S, R) hipLaunchKernelGGL((k_quant_rows<T, S, R>), dim3(g), dim3(kQT), 0, stream, (const T *)x, nblocks, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
 #define NVFP4_QCOLS(T, S, R) hipLaunchKernelGGL((k_quant_cols<T, S, R>), qtiles, dim3(kQT), 0, stream, (const T *)x, rows, cols, sign_mask, seed, offset, meta, (uint2 *)codes, scales)
 #define NVFP4_DISPATCH(MAC, T)                  \
   do {                                          \
@@ -389,6 +431,75 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
 #undef NVFP4_QROWS
 #undef NVFP4_QCOLS
 #undef NVFP4_DISPATCH
+}
+
+// Grid of the column-wise amax kernels: 256 * kCPT columns x kNBT blocks.
+dim3 col_tiles(int64_t rows, int64_t cols, bool bf16) {
+  const int64_t cpt = bf16 ? 2 : 1;
+  return dim3((unsigned)((cols + kQT * cpt - 1) / (kQT * cpt)), (unsigned)((rows / 16 + kNBT - 1) / kNBT));
+}
+
+// Plain amax of all n elements into amax_bits (and amax_bits2 if given).
+void launch_amax_flat(const void *x, bool bf16, int64_t n, uint32_t *amax_bits, uint32_t *amax_bits2,
+                      hipStream_t stream) {
+  const int64_t n16 = n * (bf16 ? 2 : 4) / 16;
+  const unsigned g = grid_for(n16, kQT * 4, 1024);
+  const int64_t per = (n16 + g - 1) / g;
+  if (bf16) hipLaunchKernelGGL(k_amax_flat<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits, amax_bits2);
+  else hipLaunchKernelGGL(k_amax_flat<float>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits, amax_bits2);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                           uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
+                           uint8_t *scales, float *meta, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  uint32_t *amax_bits = reinterpret_cast<uint32_t *>(meta);
+  hipLaunchKernelGGL(k_meta_init, dim3(1), dim3(64), 0, stream, meta);
+  if (n == 0) return hipGetLastError();
+  const bool bf16 = (x_dtype == 1);
+  const dim3 tiles = col_tiles(rows, cols, bf16);
+  if (axis == 0 && tiles.y > 65535u) return hipErrorInvalidValue;
+  // pass 1: amax
+  if (!rht) {
+    launch_amax_flat(x, bf16, n, amax_bits, nullptr, stream);
+  } else if (axis == 1) {
+    const int64_t nch = n / 16;
+    const unsigned g = grid_for(nch, kQT * 2, 2048);
+    const int64_t per = (nch + g - 1) / g;
+    if (bf16) hipLaunchKernelGGL(k_amax_rht_rows<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint16_t *)x, nch, per, sign_mask, amax_bits);
+    else hipLaunchKernelGGL(k_amax_rht_rows<float>, dim3(g), dim3(kQT), 0, stream, (const float *)x, nch, per, sign_mask, amax_bits);
+  } else {
+    if (bf16) hipLaunchKernelGGL(k_amax_rht_cols<uint16_t>, tiles, dim3(kQT), 0, stream, (const uint16_t *)x, rows, cols, sign_mask, amax_bits);
+    else hipLaunchKernelGGL(k_amax_rht_cols<float>, tiles, dim3(kQT), 0, stream, (const float *)x, rows, cols, sign_mask, amax_bits);
+  }
+  // pass 2: encode
+  launch_encode(x, bf16, rows, cols, axis, rounding, seed, offset, rht, sign_mask, codes, scales, meta, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int rounding1,
+                                uint64_t seed1, uint64_t offset1, uint8_t *codes1, uint8_t *scales1, float *meta1,
+                                bool rht0, uint32_t sign_mask0, int rounding0, uint64_t seed0, uint64_t offset0,
+                                uint8_t *codes0, uint8_t *scales0, float *meta0, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  hipLaunchKernelGGL(k_meta_init2, dim3(1), dim3(64), 0, stream, meta1, meta0);
+  if (n == 0) return hipGetLastError();
+  const bool bf16 = (x_dtype == 1);
+  const dim3 tiles = col_tiles(rows, cols, bf16);
+  if (tiles.y > 65535u) return hipErrorInvalidValue;
+  uint32_t *bits1 = reinterpret_cast<uint32_t *>(meta1), *bits0 = reinterpret_cast<uint32_t *>(meta0);
+  // pass 1: both maxima from one read
+  if (!rht0) {
+    launch_amax_flat(x, bf16, n, bits1, bits0, stream);
+  } else {
+    if (bf16) hipLaunchKernelGGL(k_amax_dual_cols<uint16_t>, tiles, dim3(kQT), 0, stream, (const uint16_t *)x, rows, cols, sign_mask0, bits1, bits0);
+    else hipLaunchKernelGGL(k_amax_dual_cols<float>, tiles, dim3(kQT), 0, stream, (const float *)x, rows, cols, sign_mask0, bits1, bits0);
+  }
+  // pass 2: the two encodes
+  launch_encode(x, bf16, rows, cols, 1, rounding1, seed1, offset1, false, 0u, codes1, scales1, meta1, stream);
+  launch_encode(x, bf16, rows, cols, 0, rounding0, seed0, offset0, rht0, sign_mask0, codes0, scales0, meta0, stream);
   return hipGetLastError();
 }
 

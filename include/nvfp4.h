@@ -124,6 +124,28 @@ int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, i
                        nvfp4_tensor *out, void *hip_stream);
 
 /*
+ * nvfp4_quantize_dual -- both layouts of one input with one amax read.  A
+ * training step needs each of its tensors quantized along both of its
+ * dimensions: dY along its columns for the data gradient and along its rows
+ * for the weight gradient ([P4] "Technologie stabilizujace ...": stochastic
+ * rounding of the gradients, the Hadamard transform for the weight
+ * gradients).  Equivalent, bit for bit, to
+ *   nvfp4_quantize(x, x_dtype, rows, cols, 1, rounding1, seed1, offset1, out1)
+ * followed by nvfp4_quantize (rht0 == 0) or nvfp4_rht_quantize (rht0 == 1)
+ * of x with axis 0, rounding0, seed0, offset0, sign_mask0 into out0; the
+ * amax pass reads x once for both maxima (the plain one, and the one after
+ * the column transform).
+ *  rows % 16 == 0 and cols % 16 == 0 (both layouts need whole blocks);
+ *  out1: outer = rows, k = cols; out0: outer = cols, k = rows; out1->meta and
+ *  out0->meta must be different words (NVFP4_ERR_SHAPE otherwise) and the
+ *  outputs must not overlap each other or x.  Enqueues four kernels.
+ */
+int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols,
+                        int rounding1, uint64_t seed1, uint64_t offset1, nvfp4_tensor *out1,
+                        int rht0, uint16_t sign_mask0, int rounding0, uint64_t seed0,
+                        uint64_t offset0, nvfp4_tensor *out0, void *hip_stream);
+
+/*
  * nvfp4_dequantize -- y[o][kk] = (e2m1(code) * e4m3(scale)) * g in binary32
  * (the first product is exact, the second rounds once); bf16 output is the
  * nearest-even rounding of that value.  y: device [q->outer][q->k] row-major

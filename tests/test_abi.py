@@ -102,3 +102,23 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(nv.NVFP4Error, match="GPU"):
         nv.nvfp4_quantize(torch.zeros(16, 32))
+
+
+@_no_gpu
+def test_quantize_dual_argument_errors(L):
+    by = ctypes.byref
+    q1, q0 = _t(16, 32), _t(32, 16, meta=FAKE + 64)
+    call = L.nvfp4_quantize_dual
+    assert call(FAKE, 1, 16, 32, 0, 0, 0, None, 0, 0, 0, 0, 0, by(q0), None) == -1       # out1 NULL
+    assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, None, None) == -1       # out0 NULL
+    assert call(FAKE, 9, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -3     # dtype
+    assert call(FAKE, 1, 16, 32, 5, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -3     # rounding1
+    assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 5, 0, 0, by(q0), None) == -3     # rounding0
+    assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q1), 2, 0, 0, 0, 0, by(q0), None) == -3     # rht0
+    q1b, q0b = _t(24, 32), _t(32, 24, meta=FAKE + 64)
+    assert call(FAKE, 1, 24, 32, 0, 0, 0, by(q1b), 0, 0, 0, 0, 0, by(q0b), None) == -2   # rows % 16
+    assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q0), 0, 0, 0, 0, 0, by(q1), None) == -2     # swapped outputs
+    qsame = _t(32, 16)
+    assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(qsame), None) == -2  # shared meta
+    assert call(None, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -1     # x NULL
+    assert call(FAKE + 2, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -5 # x misaligned
