@@ -308,6 +308,37 @@ def main():
                         "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4)}
         del T, qT, qTt
 
+    # ------------------------------------------- BF16 GEMM context ----
+    # The same three products in bf16 through torch.matmul (hipBLASLt), to
+    # state the 4-bit path's speed against a 16-bit one as a measured ratio.
+    # Context only: it is not the NVFP4 path and does not enter `value`.
+    bf16_ctx = None
+    if not args.no_sweep:
+        W1t = W1.t().contiguous()
+        X2t = X2.t().contiguous()
+        prods = {"fprop": (lambda: torch.matmul(X1, W1t), F.flops),
+                 "dgrad": (lambda: torch.matmul(dY, W2), D.flops),
+                 "wgrad": (lambda: torch.matmul(X2t, dY), Wg.flops)}
+        bf16_ctx = {}
+        tot_bf16 = 0.0
+        for name, (fn, fl) in prods.items():
+            for _ in range(2):
+                fn()
+            times = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = sorted(times)[2]
+            tot_bf16 += ms
+            bf16_ctx[name] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1)}
+        nv_gemm_ms = sum(float(np.mean(per_op[:, i])) for i, (n, _, _) in enumerate(ops) if n.startswith("gemm"))
+        bf16_ctx["gemm_time_ratio_bf16_over_nvfp4"] = round(tot_bf16 / nv_gemm_ms, 3)
+        del W1t, X2t
+
     # ------------------------------------------------- CPU baseline ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -325,6 +356,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": breakdown,
         "quantize_sweep_32768x8192_bf16": sweep,
+        "bf16_gemm_context": bf16_ctx,
         "device": torch.cuda.get_device_name(0),
         "step_ms_event_median": round(float(np.median(step_ms)), 4),
     }
