@@ -297,11 +297,14 @@ static void load_block(const void *x, int dtype, int64_t rows, int64_t cols,
  *     m_b = (S_b == 0) ? 0 : s_enc / S_b.
  *  5. per element v = Y * m_b, coded by RNE or SR (16 Philox bits).
  *  6. two codes per byte, even element in the low nibble.
- * Output layout: codes[o][K/2], scales[o][K/16], meta[2]. */
+ * Output layout: codes[o][K/2], scales[o][K/16], meta[2].
+ * amax_in: NULL, or a supplied tensor amax that replaces step 2 (the scale
+ * level the producer of x already knows; a smaller value than the true
+ * maximum saturates: block scales at 448, codes at 6). */
 int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
                     int axis, int rounding, uint64_t seed, uint64_t offset,
-                    int rht, uint32_t sign_mask, uint8_t *codes,
-                    uint8_t *scales, float *meta)
+                    int rht, uint32_t sign_mask, const float *amax_in,
+                    uint8_t *codes, uint8_t *scales, float *meta)
 {
     if (rows < 0 || cols < 0) return -2;
     int64_t outer = axis ? rows : cols;
@@ -309,10 +312,10 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
     if (K % 16 != 0) return -2;
     int64_t nb = K / 16;
 
-    /* step 2: tensor amax */
+    /* step 2: tensor amax (unless supplied) */
     uint32_t amax_bits = 0;
 #pragma omp parallel for reduction(max : amax_bits) schedule(static)
-    for (int64_t o = 0; o < outer; ++o) {
+    for (int64_t o = 0; o < (amax_in ? 0 : outer); ++o) {
         for (int64_t b = 0; b < nb; ++b) {
             float y[16];
             load_block(x, dtype, rows, cols, axis, rht, sign_mask, o, b, y);
@@ -322,7 +325,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
             }
         }
     }
-    float amax = bits_f32(amax_bits);
+    float amax = amax_in ? *amax_in : bits_f32(amax_bits);
 
     /* step 3: tensor scales */
     float s_enc, kk, g;
