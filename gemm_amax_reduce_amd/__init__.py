@@ -15,7 +15,8 @@ import os
 
 import torch
 
-__all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual",
+__all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_amax",
+           "nvfp4_quantize_amax",
            "nvfp4_dequantize", "nvfp4_gemm", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,8 +38,8 @@ class _CTensor(ctypes.Structure):
 _lib = None
 
 # every symbol the header declares
-EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_dequantize", "nvfp4_gemm",
-           "nvfp4_status_string")
+EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_quantize_dual",
+           "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -55,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize.restype = ci
         L.nvfp4_rht_quantize.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, ctypes.c_uint16, pt, vp]
         L.nvfp4_rht_quantize.restype = ci
+        L.nvfp4_amax.argtypes = [vp, ci, i64, i64, ci, ci, ctypes.c_uint16, vp, vp]
+        L.nvfp4_amax.restype = ci
+        L.nvfp4_quantize_amax.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, ci, ctypes.c_uint16, vp, pt, vp]
+        L.nvfp4_quantize_amax.restype = ci
         L.nvfp4_quantize_dual.argtypes = [vp, ci, i64, i64, ci, u64, u64, pt, ci, ctypes.c_uint16, ci, u64, u64,
                                           pt, vp]
         L.nvfp4_quantize_dual.restype = ci
@@ -152,6 +157,41 @@ def nvfp4_rht_quantize(x: torch.Tensor, sign_mask: int, axis: int = 1, rounding=
                        offset: int = 0, out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
     """Quantize after the 16-point random Hadamard transform along k."""
     return _quantize(x, axis, rounding, seed, offset, True, sign_mask, out, stream)
+
+
+def nvfp4_amax(x: torch.Tensor, axis: int = 1, rht: bool = False, sign_mask: int = 0,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The tensor amax of x on `axis` (after the RHT if rht), as f32 [1] on x's device."""
+    _require_device(x, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise NVFP4Error("x must be a contiguous 2-D tensor")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    rows, cols = x.shape
+    _check(lib().nvfp4_amax(x.data_ptr(), _dtype_code(x), rows, cols, axis, int(bool(rht)), sign_mask & 0xFFFF,
+                            out.data_ptr(), _stream_handle(stream)), "nvfp4_amax")
+    return out
+
+
+def nvfp4_quantize_amax(x: torch.Tensor, amax: torch.Tensor, axis: int = 1, rounding="rne", seed: int = 0,
+                        offset: int = 0, rht: bool = False, sign_mask: int = 0,
+                        out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """Quantize with the tensor amax supplied (device f32, element 0)."""
+    _require_device(x, "x")
+    _require_device(amax, "amax")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise NVFP4Error("x must be a contiguous 2-D tensor")
+    if amax.dtype != torch.float32 or amax.numel() < 1:
+        raise NVFP4Error("amax must be a float32 tensor with at least one element")
+    rows, cols = x.shape
+    outer, k = (rows, cols) if axis == 1 else (cols, rows)
+    if out is None:
+        out = NVFP4Tensor.empty(outer, k, device=x.device)
+    ct = out._c()
+    _check(lib().nvfp4_quantize_amax(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding), seed,
+                                     offset, int(bool(rht)), sign_mask & 0xFFFF, amax.data_ptr(), ctypes.byref(ct),
+                                     _stream_handle(stream)), "nvfp4_quantize_amax")
+    return out
 
 
 def nvfp4_quantize_dual(x: torch.Tensor, rounding1="rne", seed1: int = 0, offset1: int = 0,

@@ -53,6 +53,42 @@ int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, i
   return quantize_common(x, x_dtype, rows, cols, axis, rounding, seed, offset, true, sign_mask, out, hip_stream);
 }
 
+int nvfp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rht, uint16_t sign_mask,
+               float *amax, void *hip_stream) {
+  if (!amax) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
+  if (rht != 0 && rht != 1) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if ((axis ? cols : rows) % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_amax(x, x_dtype, rows, cols, axis, rht != 0, sign_mask, amax,
+                                       (hipStream_t)hip_stream));
+}
+
+int nvfp4_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                        uint64_t seed, uint64_t offset, int rht, uint16_t sign_mask, const float *amax,
+                        nvfp4_tensor *out, void *hip_stream) {
+  if (!out || !amax) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_ENUM;
+  if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
+  if (rht != 0 && rht != 1) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  const int64_t outer = axis ? rows : cols;
+  const int64_t k = axis ? cols : rows;
+  if (k % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
+  int st = check_tensor(out);
+  if (st != NVFP4_OK) return st;
+  if (!aligned(x, 16) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_quantize_amax(x, x_dtype, rows, cols, axis, rounding, seed, offset, rht != 0,
+                                                sign_mask, amax, out->codes, out->scales, out->meta,
+                                                (hipStream_t)hip_stream));
+}
+
 int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int rounding1, uint64_t seed1,
                         uint64_t offset1, nvfp4_tensor *out1, int rht0, uint16_t sign_mask0, int rounding0,
                         uint64_t seed0, uint64_t offset0, nvfp4_tensor *out0, void *hip_stream) {

@@ -15,6 +15,15 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
                            uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
                            uint8_t *scales, float *meta, hipStream_t stream);
 
+// Pass 1 alone: amax[0] = the tensor amax (after the transform if rht).
+hipError_t launch_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, bool rht,
+                       uint32_t sign_mask, float *amax, hipStream_t stream);
+
+// Pass 2 alone, with the tensor amax supplied in device memory.
+hipError_t launch_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                                uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, const float *amax,
+                                uint8_t *codes, uint8_t *scales, float *meta, hipStream_t stream);
+
 // One input, two quantizations with one amax read: the axis-1 output (no
 // transform) and the axis-0 output (with or without the RHT); each output is
 // bit-identical to launch_quantize's.

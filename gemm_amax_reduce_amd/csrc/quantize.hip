@@ -90,6 +90,18 @@ __global__ void k_meta_init(float *meta) {
   }
 }
 
+// meta = {supplied amax, 0}: the encode pass reads meta[0] and writes meta[1].
+__global__ void k_meta_set(float *meta, const float *amax) {
+  if (threadIdx.x == 0) {
+    meta[0] = amax[0];
+    meta[1] = 0.0f;
+  }
+}
+
+__global__ void k_zero1(float *v) {
+  if (threadIdx.x == 0) v[0] = 0.0f;
+}
+
 __global__ void k_meta_init2(float *meta_a, float *meta_b) {
   if (threadIdx.x == 0) {
     meta_a[0] = 0.0f;
@@ -449,19 +461,11 @@ void launch_amax_flat(const void *x, bool bf16, int64_t n, uint32_t *amax_bits, 
   else hipLaunchKernelGGL(k_amax_flat<float>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits, amax_bits2);
 }
 
-}  // namespace
-
-hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
-                           uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
-                           uint8_t *scales, float *meta, hipStream_t stream) {
+// Pass 1 of a quantization: the tensor amax (after the transform if rht)
+// folded into *amax_bits, which must start at zero.
+void launch_pass1(const void *x, bool bf16, int64_t rows, int64_t cols, int axis, bool rht, uint32_t sign_mask,
+                  uint32_t *amax_bits, hipStream_t stream) {
   const int64_t n = rows * cols;
-  uint32_t *amax_bits = reinterpret_cast<uint32_t *>(meta);
-  hipLaunchKernelGGL(k_meta_init, dim3(1), dim3(64), 0, stream, meta);
-  if (n == 0) return hipGetLastError();
-  const bool bf16 = (x_dtype == 1);
-  const dim3 tiles = col_tiles(rows, cols, bf16);
-  if (axis == 0 && tiles.y > 65535u) return hipErrorInvalidValue;
-  // pass 1: amax
   if (!rht) {
     launch_amax_flat(x, bf16, n, amax_bits, nullptr, stream);
   } else if (axis == 1) {
@@ -471,9 +475,46 @@ hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
     if (bf16) hipLaunchKernelGGL(k_amax_rht_rows<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint16_t *)x, nch, per, sign_mask, amax_bits);
     else hipLaunchKernelGGL(k_amax_rht_rows<float>, dim3(g), dim3(kQT), 0, stream, (const float *)x, nch, per, sign_mask, amax_bits);
   } else {
+    const dim3 tiles = col_tiles(rows, cols, bf16);
     if (bf16) hipLaunchKernelGGL(k_amax_rht_cols<uint16_t>, tiles, dim3(kQT), 0, stream, (const uint16_t *)x, rows, cols, sign_mask, amax_bits);
     else hipLaunchKernelGGL(k_amax_rht_cols<float>, tiles, dim3(kQT), 0, stream, (const float *)x, rows, cols, sign_mask, amax_bits);
   }
+}
+
+}  // namespace
+
+hipError_t launch_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, bool rht,
+                       uint32_t sign_mask, float *amax, hipStream_t stream) {
+  hipLaunchKernelGGL(k_zero1, dim3(1), dim3(64), 0, stream, amax);
+  if (rows * cols == 0) return hipGetLastError();
+  const bool bf16 = (x_dtype == 1);
+  if (axis == 0 && col_tiles(rows, cols, bf16).y > 65535u) return hipErrorInvalidValue;
+  launch_pass1(x, bf16, rows, cols, axis, rht, sign_mask, reinterpret_cast<uint32_t *>(amax), stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                                uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, const float *amax,
+                                uint8_t *codes, uint8_t *scales, float *meta, hipStream_t stream) {
+  hipLaunchKernelGGL(k_meta_set, dim3(1), dim3(64), 0, stream, meta, amax);
+  if (rows * cols == 0) return hipGetLastError();
+  const bool bf16 = (x_dtype == 1);
+  if (axis == 0 && col_tiles(rows, cols, bf16).y > 65535u) return hipErrorInvalidValue;
+  launch_encode(x, bf16, rows, cols, axis, rounding, seed, offset, rht, sign_mask, codes, scales, meta, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
+                           uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, uint8_t *codes,
+                           uint8_t *scales, float *meta, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  uint32_t *amax_bits = reinterpret_cast<uint32_t *>(meta);
+  hipLaunchKernelGGL(k_meta_init, dim3(1), dim3(64), 0, stream, meta);
+  if (n == 0) return hipGetLastError();
+  const bool bf16 = (x_dtype == 1);
+  if (axis == 0 && col_tiles(rows, cols, bf16).y > 65535u) return hipErrorInvalidValue;
+  // pass 1: amax
+  launch_pass1(x, bf16, rows, cols, axis, rht, sign_mask, amax_bits, stream);
   // pass 2: encode
   launch_encode(x, bf16, rows, cols, axis, rounding, seed, offset, rht, sign_mask, codes, scales, meta, stream);
   return hipGetLastError();

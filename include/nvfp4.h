@@ -124,6 +124,30 @@ int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, i
                        nvfp4_tensor *out, void *hip_stream);
 
 /*
+ * nvfp4_amax -- the first pass of a quantization alone: *amax = the tensor
+ * amax of x viewed on `axis` (after the 16-point transform along k when
+ * rht == 1, with sign_mask as in nvfp4_rht_quantize), the maximum of |value|
+ * taken on IEEE bit patterns (exact; NaN > Inf > finite).  0 for an empty
+ * tensor.  amax: device, one f32, 4-byte aligned.  Enqueues two kernels.
+ *
+ * nvfp4_quantize_amax -- the second pass alone: as nvfp4_quantize (rht == 0)
+ * or nvfp4_rht_quantize (rht == 1) with the tensor amax read from device
+ * memory instead of computed, which saves the first read of x when the
+ * producer of x already knows its maximum ([P4] "Architektura NVFP4 ...":
+ * the FP32 tensor-level scale).  out->meta becomes {*amax, *amax / 2688}.
+ * *amax must be finite and >= 0 (not checked): with the true maximum the
+ * result equals nvfp4_quantize's bit for bit; a smaller value saturates
+ * (block scales at 448, codes at 6), so the decoded values are clipped to
+ * +-*amax.  Enqueues two kernels.
+ */
+int nvfp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rht,
+               uint16_t sign_mask, float *amax, void *hip_stream);
+int nvfp4_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis,
+                        int rounding, uint64_t seed, uint64_t offset, int rht,
+                        uint16_t sign_mask, const float *amax, nvfp4_tensor *out,
+                        void *hip_stream);
+
+/*
  * nvfp4_quantize_dual -- both layouts of one input with one amax read.  A
  * training step needs each of its tensors quantized along both of its
  * dimensions: dY along its columns for the data gradient and along its rows

@@ -122,3 +122,24 @@ def test_quantize_dual_argument_errors(L):
     assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(qsame), None) == -2  # shared meta
     assert call(None, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -1     # x NULL
     assert call(FAKE + 2, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -5 # x misaligned
+
+
+@_no_gpu
+def test_amax_and_quantize_amax_argument_errors(L):
+    by = ctypes.byref
+    assert L.nvfp4_amax(FAKE, 1, 16, 32, 1, 0, 0, None, None) == -1           # amax NULL
+    assert L.nvfp4_amax(FAKE, 4, 16, 32, 1, 0, 0, FAKE, None) == -3           # dtype
+    assert L.nvfp4_amax(FAKE, 1, 16, 32, 3, 0, 0, FAKE, None) == -3           # axis
+    assert L.nvfp4_amax(FAKE, 1, 16, 32, 1, 2, 0, FAKE, None) == -3           # rht
+    assert L.nvfp4_amax(FAKE, 1, 16, 24, 1, 0, 0, FAKE, None) == -2           # K % 16 (axis 1: cols)
+    assert L.nvfp4_amax(FAKE, 1, 24, 32, 0, 0, 0, FAKE, None) == -2           # K % 16 (axis 0: rows)
+    assert L.nvfp4_amax(None, 1, 16, 32, 1, 0, 0, FAKE, None) == -1           # x NULL
+    assert L.nvfp4_amax(FAKE, 1, 16, 32, 1, 0, 0, FAKE + 2, None) == -5       # amax misaligned
+    q = _t(16, 32)
+    call = L.nvfp4_quantize_amax
+    assert call(FAKE, 1, 16, 32, 1, 0, 0, 0, 0, 0, None, by(q), None) == -1   # amax NULL
+    assert call(FAKE, 1, 16, 32, 1, 0, 0, 0, 0, 0, FAKE, None, None) == -1    # out NULL
+    assert call(FAKE, 1, 16, 32, 1, 3, 0, 0, 0, 0, FAKE, by(q), None) == -3   # rounding
+    assert call(FAKE, 1, 16, 32, 1, 0, 0, 0, 5, 0, FAKE, by(q), None) == -3   # rht
+    assert call(FAKE, 1, 16, 32, 0, 0, 0, 0, 0, 0, FAKE, by(q), None) == -2   # axis-0 view is 32x16
+    assert call(FAKE, 1, 16, 32, 1, 0, 0, 0, 0, 0, FAKE + 1, by(q), None) == -5
