@@ -1,0 +1,91 @@
+"""NVFP4 linear layer over the C ABI: forward and backward of y = x W^T with
+every product on the block-scaled NVFP4 GEMM.
+
+The recipe follows the pages: [P4] aisight.pl "Koniec marnowania mocy ...",
+section "Technologie stabilizujace proces treningowy" (stochastic rounding of
+the gradients, the 16-point random Hadamard transform on the weight-gradient
+operands, a share of the last layers kept in BF16) and [P3]
+aibuzzwire.news "End-to-End 4-Bit Training", section "Unterschiedliche
+Phasen, unterschiedliche Regeln" (nearest rounding in the forward pass,
+stochastic rounding of the gradients).
+
+    forward  y  = x W^T    A = x (axis 1, RNE),  B = W (axis 1, RNE)
+    backward dx = dy W     A = dy (axis 1, SR),  B = W (axis 0, RNE)
+             dW = dy^T x   A = dy (axis 0, RHT, SR), B = x (axis 0, RHT, RNE)
+
+dy's two quantizations come from one dual-layout call.  The two operands of
+the weight gradient share one sign mask, so the transform cancels in the
+product.  Every quantization and GEMM runs in the HIP library; there is no
+CPU path.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (nvfp4_gemm, nvfp4_quantize, nvfp4_quantize_dual, nvfp4_rht_quantize, NVFP4Error)
+
+
+class NVFP4LinearFunction(torch.autograd.Function):
+    """y = x W^T for x [tokens, in], W [out, in]; returns y in x's dtype."""
+
+    @staticmethod
+    def forward(ctx, x, weight, seed: int, offset: int, sign_mask: int):
+        if x.dim() != 2 or weight.dim() != 2 or x.shape[1] != weight.shape[1]:
+            raise NVFP4Error("x must be [tokens, in] and weight [out, in]")
+        x = x.contiguous()
+        weight = weight.contiguous()
+        qx = nvfp4_quantize(x, axis=1)
+        qw = nvfp4_quantize(weight, axis=1)
+        out_dtype = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
+        y = nvfp4_gemm(qx, qw, out_dtype)
+        ctx.save_for_backward(x, weight)
+        ctx.seed, ctx.offset, ctx.sign_mask = seed, offset, sign_mask
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, weight = ctx.saved_tensors
+        dy = dy.contiguous().to(x.dtype)
+        # dy along its columns (data gradient) and, transformed, along its
+        # rows (weight gradient); distinct Philox offsets keep the two draws
+        # independent
+        qdy1, qdy0 = nvfp4_quantize_dual(dy, rounding1="sr", seed1=ctx.seed, offset1=2 * ctx.offset,
+                                         rht0=True, sign_mask0=ctx.sign_mask, rounding0="sr", seed0=ctx.seed,
+                                         offset0=2 * ctx.offset + 1)
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            qw0 = nvfp4_quantize(weight, axis=0)
+            dx = nvfp4_gemm(qdy1, qw0, torch.float32).to(x.dtype)
+        if ctx.needs_input_grad[1]:
+            qx0 = nvfp4_rht_quantize(x, ctx.sign_mask, axis=0)
+            dw = nvfp4_gemm(qdy0, qx0, torch.float32).to(weight.dtype)
+        return dx, dw, None, None, None
+
+
+class NVFP4Linear(torch.nn.Module):
+    """Bias-free linear layer whose products run in NVFP4.
+
+    keep_bf16=True runs the layer as a plain bf16 linear instead: the pages
+    keep a share of the final layers in BF16 (the caller decides which).
+    Each forward call draws a fresh Philox offset, so successive steps use
+    independent stochastic rounding.
+    """
+
+    def __init__(self, in_features: int, out_features: int, seed: int = 0, sign_mask: int = 0xA5C3,
+                 keep_bf16: bool = False, device=None, dtype=torch.bfloat16):
+        super().__init__()
+        if in_features % 16 or out_features % 16:
+            raise NVFP4Error("in_features and out_features must be multiples of 16")
+        self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device, dtype=dtype))
+        torch.nn.init.normal_(self.weight, std=0.02)
+        self.seed, self.sign_mask, self.keep_bf16 = seed, sign_mask & 0xFFFF, keep_bf16
+        self._calls = 0
+
+    def forward(self, x):
+        if self.keep_bf16:
+            return torch.nn.functional.linear(x.to(torch.bfloat16), self.weight.to(torch.bfloat16)).to(x.dtype)
+        if x.shape[0] % 16:
+            raise NVFP4Error("the token count must be a multiple of 16 (the weight gradient reduces over it)")
+        offset = self._calls
+        self._calls += 1
+        return NVFP4LinearFunction.apply(x, self.weight, self.seed, offset, self.sign_mask)

@@ -1,0 +1,88 @@
+"""GPU checks of the NVFP4 linear layer (autograd over the C ABI): forward and
+both gradients against the oracle's quantizations and fp64 GEMM of the same
+operands, within the GEMM tolerance 1e-5 * sum|a*b| (bf16 outputs by the
+rounding interval), and the BF16 policy flag equal to a plain bf16 linear."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+MASK = 0xA5C3
+
+
+def _ref(qa, qb):
+    c, bound = oracle.gemm(qa, qb)
+    return c, bound
+
+
+def _close_f32(got, c, bound, label):
+    ok, worst = oracle.check_gemm_f32(got, c, bound, 1e-5)
+    assert ok, f"{label}: worst |err|/bound = {worst:.3e}"
+
+
+def _within_bf16(got_bf16, c, bound, label):
+    ok, nbad = oracle.check_gemm_bf16(got_bf16.double().cpu().numpy(), c, bound, 1e-5)
+    assert ok, f"{label}: {nbad} bf16 outputs outside the tolerance interval"
+
+
+def test_forward_and_backward_match_oracle():
+    import gemm_amax_reduce_amd.linear as L
+    tokens, fin, fout = 64, 96, 80
+    print(f"[linear] {tokens}x{fin} -> {fout}", flush=True)
+    torch.manual_seed(0)
+    layer = L.NVFP4Linear(fin, fout, seed=3, sign_mask=MASK, device="cuda", dtype=torch.float32)
+    x = torch.from_numpy(workloads.normal(tokens, fin, 5)).cuda().requires_grad_(True)
+    y = layer(x)
+    dy = torch.from_numpy(workloads.laplace(tokens, fout, 6, 1e-3)).cuda()
+    y.backward(dy)
+    torch.cuda.synchronize()
+    xc, wc, dyc = x.detach().cpu(), layer.weight.detach().cpu(), dy.cpu()
+    # forward
+    c, b = _ref(oracle.quantize(xc, axis=1), oracle.quantize(wc, axis=1))
+    _close_f32(y.detach().cpu().numpy(), c, b, "y")
+    # data gradient: dy (axis 1, SR, offset 0) . W (axis 0)
+    c, b = _ref(oracle.quantize(dyc, axis=1, rounding=oracle.SR, seed=3, offset=0), oracle.quantize(wc, axis=0))
+    _close_f32(x.grad.cpu().numpy(), c, b, "dx")
+    # weight gradient: dy (axis 0, RHT, SR, offset 1) . x (axis 0, RHT)
+    c, b = _ref(oracle.quantize(dyc, axis=0, rounding=oracle.SR, seed=3, offset=1, rht=True, sign_mask=MASK),
+                oracle.quantize(xc, axis=0, rht=True, sign_mask=MASK))
+    _close_f32(layer.weight.grad.cpu().numpy(), c, b, "dW")
+
+
+def test_bf16_forward_output():
+    import gemm_amax_reduce_amd.linear as L
+    layer = L.NVFP4Linear(64, 48, device="cuda", dtype=torch.bfloat16)
+    x = workloads.to_bf16(workloads.normal(32, 64, 8)).cuda()
+    y = layer(x)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16
+    c, b = _ref(oracle.quantize(x.cpu(), axis=1), oracle.quantize(layer.weight.detach().cpu(), axis=1))
+    _within_bf16(y.detach(), c, b, "y bf16")
+
+
+def test_keep_bf16_policy_is_plain_linear():
+    import gemm_amax_reduce_amd.linear as L
+    layer = L.NVFP4Linear(64, 32, keep_bf16=True, device="cuda", dtype=torch.bfloat16)
+    x = workloads.to_bf16(workloads.normal(16, 64, 9)).cuda()
+    y = layer(x)
+    ref = torch.nn.functional.linear(x.float(), layer.weight.detach().float())
+    torch.cuda.synchronize()
+    assert torch.allclose(y.detach().float(), ref, rtol=2e-2, atol=1e-2)
+
+
+def test_successive_calls_draw_fresh_offsets():
+    import gemm_amax_reduce_amd.linear as L
+    layer = L.NVFP4Linear(64, 32, seed=1, device="cuda", dtype=torch.float32)
+    x = torch.from_numpy(workloads.normal(32, 64, 10)).cuda().requires_grad_(True)
+    dy = torch.from_numpy(workloads.laplace(32, 32, 11, 1e-3)).cuda()   # off-grid values: SR has work
+    grads = []
+    for _ in range(2):
+        x.grad = None
+        layer(x).backward(dy)
+        grads.append(x.grad.clone())
+    torch.cuda.synchronize()
+    assert not torch.equal(grads[0], grads[1])     # stochastic rounding differs between steps
