@@ -84,6 +84,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_dequantize.restype = ctypes.c_int
         L.oracle_decode_qs.argtypes = [vp, vp, c_i64, vp, c_i64, vp]
         L.oracle_decode_qs.restype = ctypes.c_int
+        L.oracle_mx_scale_exp.argtypes = [c_u32]
+        L.oracle_mx_scale_exp.restype = ctypes.c_int
+        L.oracle_mxfp4_quantize.argtypes = [vp, ctypes.c_int, c_i64, c_i64, ctypes.c_int, vp, vp]
+        L.oracle_mxfp4_quantize.restype = ctypes.c_int
+        L.oracle_mxfp4_decode.argtypes = [vp, vp, c_i64, vp, c_i64, vp]
+        L.oracle_mxfp4_decode.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -277,3 +283,58 @@ def check_gemm_bf16(c_gpu_bf16_as_f64: np.ndarray, c_ref: np.ndarray, bound: np.
     c = np.asarray(c_gpu_bf16_as_f64, dtype=np.float64)
     ok = bool(np.all((c >= lo) & (c <= hi)))
     return ok, int(np.sum(~((c >= lo) & (c <= hi))))
+
+
+# --------------------------------------------------------------- MXFP4 ----
+
+class MXQuantized:
+    """An MXFP4 tensor in its quantized [outer][k] layout: codes u8
+    [outer, k/2] (element 2j in the low nibble), scales u8 [outer, k/32]
+    (E8M0: 2^(code - 127))."""
+
+    def __init__(self, codes, scales, outer, k):
+        self.codes, self.scales, self.outer, self.k = codes, scales, outer, k
+
+
+def mx_scale_exp(amax: float) -> int:
+    """Exponent e of the MXFP4 block scale for a block maximum amax >= 0."""
+    bits = int(np.array([amax], dtype=np.float32).view(np.uint32)[0])
+    return lib().oracle_mx_scale_exp(bits)
+
+
+def mxfp4_quantize(x, axis: int = 1) -> MXQuantized:
+    a, dt = _as_raw(x)
+    a = np.ascontiguousarray(a)
+    rows, cols = a.shape
+    outer, K = (rows, cols) if axis else (cols, rows)
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    codes = np.zeros((outer, K // 2), dtype=np.uint8)
+    scales = np.zeros((outer, K // 32), dtype=np.uint8)
+    rc = lib().oracle_mxfp4_quantize(_ptr(a), dt, rows, cols, axis, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp4_quantize failed: {rc}")
+    return MXQuantized(codes, scales, outer, K)
+
+
+def mxfp4_decode(q: MXQuantized, rows=None) -> np.ndarray:
+    """Exact values q * 2^e of the selected outer rows, float64 [n][K]."""
+    if rows is None:
+        rows = np.arange(q.outer, dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.zeros((rows.size, q.k), dtype=np.float64)
+    rc = lib().oracle_mxfp4_decode(_ptr(q.codes), _ptr(q.scales), q.k, _ptr(rows), rows.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp4_decode failed: {rc}")
+    return out
+
+
+def mxfp4_gemm(qa: MXQuantized, qb: MXQuantized, rows=None, cols=None):
+    """C = A B^T of the decoded MXFP4 operands in float64 (every product is
+    exact), with bound = sum_k |a b| for the tolerance."""
+    if qa.k != qb.k:
+        raise ValueError("K mismatch")
+    da = mxfp4_decode(qa, rows)
+    db = mxfp4_decode(qb, cols)
+    return da @ db.T, np.abs(da) @ np.abs(db).T
+

@@ -427,3 +427,79 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------- MXFP4 ----
+ * The microscaling format the pages set NVFP4 against ([P4] "Architektura
+ * NVFP4 kontra ograniczenia mikroskalowania": blocks of 32 elements sharing
+ * a power-of-two scale; the comparison with MXFP4 in the same article's
+ * closing section).  Elements are E2M1 as for NVFP4; each 32-block along K
+ * carries one 8-bit biased exponent (E8M0: scale = 2^(code - 127)); there is
+ * no tensor-level scale.
+ * Readings (the pages give no formula): the block scale is the smallest
+ * power of two X = 2^e with amax_b / X <= 6, so the block maximum is never
+ * clipped, e clamped to [-127, 127]; an all-zero block takes e = -127.
+ * Elements are the nearest-even E2M1 code of x / X (exact: X is a power of
+ * two), codes packed two per byte as for NVFP4. */
+
+/* Smallest e with amax <= 6 * 2^e, from the bit pattern of amax >= 0.
+ * 6 * 2^e = 1.5 * 2^(e+2): for amax = m * 2^E (m in [1,2)) that is e = E - 2
+ * when m <= 1.5, else e = E - 1.  Subnormal amax fits e = -127. */
+int oracle_mx_scale_exp(uint32_t amax_bits)
+{
+    amax_bits &= 0x7FFFFFFFu;
+    if (amax_bits < 0x00800000u) return -127;          /* zero or subnormal */
+    int E = (int)(amax_bits >> 23) - 127;
+    uint32_t mant = amax_bits & 0x7FFFFFu;
+    int e = (mant <= 0x400000u) ? E - 2 : E - 1;        /* m <= 1.5 ? */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+int oracle_mxfp4_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
+                          int axis, uint8_t *codes, uint8_t *scales)
+{
+    if (rows < 0 || cols < 0) return -2;
+    int64_t outer = axis ? rows : cols;
+    int64_t K = axis ? cols : rows;
+    if (K % 32 != 0) return -2;
+    int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < outer; ++o) {
+        for (int64_t b = 0; b < nb; ++b) {
+            float y[32];
+            uint32_t bmax = 0;
+            for (int j = 0; j < 32; ++j) {
+                y[j] = view_get(x, dtype, rows, cols, axis, o, 32 * b + j);
+                uint32_t a = f32_bits(y[j]) & 0x7FFFFFFFu;
+                if (a > bmax) bmax = a;
+            }
+            int e = oracle_mx_scale_exp(bmax);
+            scales[o * nb + b] = (uint8_t)(e + 127);
+            uint8_t q[32];
+            for (int j = 0; j < 32; ++j)
+                q[j] = oracle_e2m1_rne((float)ldexp((double)y[j], -e));
+            for (int j = 0; j < 16; ++j)
+                codes[o * (K / 2) + 16 * b + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+        }
+    }
+    return 0;
+}
+
+/* Exact value q * 2^(code - 127) of the selected outer rows, as doubles. */
+int oracle_mxfp4_decode(const uint8_t *codes, const uint8_t *scales, int64_t K,
+                        const int64_t *rows_sel, int64_t n_sel, double *out)
+{
+    if (K < 0 || K % 32 != 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_sel; ++r) {
+        int64_t o = rows_sel[r];
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = codes[o * (K / 2) + k / 2];
+            uint8_t q = (k & 1) ? (byte >> 4) : (byte & 15);
+            int e = (int)scales[o * (K / 32) + k / 32] - 127;
+            out[r * K + k] = ldexp((double)oracle_e2m1_value(q), e);
+        }
+    }
+    return 0;
+}
