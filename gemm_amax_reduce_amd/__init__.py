@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_amax",
-           "nvfp4_quantize_amax",
+           "nvfp4_quantize_amax", "MXFP4Tensor", "mxfp4_quantize", "mxfp4_gemm",
            "nvfp4_dequantize", "nvfp4_gemm", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,11 +35,16 @@ class _CTensor(ctypes.Structure):
                 ("outer", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
+class _MXTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("outer", ctypes.c_int64),
+                ("k", ctypes.c_int64)]
+
+
 _lib = None
 
 # every symbol the header declares
 EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_quantize_dual",
-           "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string")
+           "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -56,6 +61,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize.restype = ci
         L.nvfp4_rht_quantize.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, ctypes.c_uint16, pt, vp]
         L.nvfp4_rht_quantize.restype = ci
+        mt = ctypes.POINTER(_MXTensor)
+        L.mxfp4_quantize.argtypes = [vp, ci, i64, i64, ci, mt, vp]
+        L.mxfp4_quantize.restype = ci
+        L.mxfp4_gemm.argtypes = [mt, mt, vp, ci, i64, vp]
+        L.mxfp4_gemm.restype = ci
         L.nvfp4_amax.argtypes = [vp, ci, i64, i64, ci, ci, ctypes.c_uint16, vp, vp]
         L.nvfp4_amax.restype = ci
         L.nvfp4_quantize_amax.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, ci, ctypes.c_uint16, vp, pt, vp]
@@ -242,3 +252,51 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: tor
     _check(lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
                             _stream_handle(stream)), "nvfp4_gemm")
     return out
+
+
+class MXFP4Tensor:
+    """Device buffers of one MXFP4 tensor in its quantized [outer][k] layout:
+    ``codes`` u8 [outer, k/2], ``scales`` u8 [outer, k/32] (E8M0)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, outer: int, k: int):
+        self.codes, self.scales, self.outer, self.k = codes, scales, int(outer), int(k)
+
+    @classmethod
+    def empty(cls, outer: int, k: int, device=None) -> "MXFP4Tensor":
+        device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        return cls(torch.empty((outer, k // 2), dtype=torch.uint8, device=device),
+                   torch.empty((outer, k // 32), dtype=torch.uint8, device=device), outer, k)
+
+    def _c(self) -> _MXTensor:
+        return _MXTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.outer, self.k)
+
+
+def mxfp4_quantize(x: torch.Tensor, axis: int = 1, out: MXFP4Tensor | None = None, stream=None) -> MXFP4Tensor:
+    """Quantize a 2-D f32/bf16 GPU tensor to MXFP4 (see include/nvfp4.h)."""
+    _require_device(x, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise NVFP4Error("x must be a contiguous 2-D tensor")
+    rows, cols = x.shape
+    outer, k = (rows, cols) if axis == 1 else (cols, rows)
+    if out is None:
+        out = MXFP4Tensor.empty(outer, k, device=x.device)
+    ct = out._c()
+    _check(lib().mxfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, ctypes.byref(ct),
+                                _stream_handle(stream)), "mxfp4_quantize")
+    return out
+
+
+def mxfp4_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """C = A . B^T for MXFP4 A [M, K] and B [N, K] (K % 256 == 0), f32 accumulation."""
+    code = F32 if out_dtype == torch.float32 else BF16
+    if out is None:
+        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=a.codes.device)
+    if out.dim() != 2 or out.stride(1) != 1:
+        raise NVFP4Error("out must be a row-major 2-D tensor")
+    ldc = out.stride(0) if out.shape[0] > 1 else max(out.shape[1], 1)
+    ca, cb = a._c(), b._c()
+    _check(lib().mxfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc, _stream_handle(stream)),
+           "mxfp4_gemm")
+    return out
+

@@ -112,6 +112,33 @@ int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
                                                 (hipStream_t)hip_stream));
 }
 
+int mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, mxfp4_tensor *out,
+                   void *hip_stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  const int64_t outer = axis ? rows : cols, k = axis ? cols : rows;
+  if (k % 32 != 0 || out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (!x || !out->codes || !out->scales)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out->codes, 16)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_mx_quantize(x, x_dtype, rows, cols, axis, out->codes, out->scales,
+                                              (hipStream_t)hip_stream));
+}
+
+int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int c_dtype, int64_t ldc, void *hip_stream) {
+  if (!a || !b) return NVFP4_ERR_NULL;
+  if (a->outer < 0 || b->outer < 0 || a->k < 0 || a->k != b->k || a->k % 256 != 0) return NVFP4_ERR_SHAPE;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  const int64_t M = a->outer, N = b->outer;
+  if (ldc < N) return NVFP4_ERR_SHAPE;
+  if (M > 0 && N > 0 && (!c || (a->k > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
+    return NVFP4_ERR_NULL;
+  if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_mx_gemm(a->codes, a->scales, b->codes, b->scales, M, N, a->k, c, c_dtype, ldc,
+                                          (hipStream_t)hip_stream));
+}
+
 int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stream) {
   int st = check_tensor(q);
   if (st != NVFP4_OK) return st;

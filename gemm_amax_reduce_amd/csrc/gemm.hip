@@ -47,6 +47,7 @@
 // round-robin to the eight XCDs (pid % 8); the tile index is remapped so each
 // XCD works on a contiguous range of tiles, ordered in groups of 8 tile rows,
 // so the tiles resident on one XCD share A rows and B columns in its L2.
+#include "gemm_common.h"
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -64,26 +65,8 @@ constexpr int kRowsMax = BM + 256;                  // operand rows of the wides
 constexpr int kCodeBytes = kRowsMax * 128;          // 64 KB of codes per group buffer
 constexpr int kGroupBytes = kCodeBytes + kRowsMax * 16;
 constexpr int kGroupM = 8;                          // tile rows per L2 group
-constexpr int kXcds = 8;
-constexpr uint32_t kOutOfRange = 0x80000000u;       // buffer offset past every view
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
-  // 0x00020000: 32-bit data format word of a raw (stride 0) buffer on gfx9.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-// 16 bytes per lane from a buffer view into LDS at dst + 16 * lane (the
-// gfx950 DMA form of buffer_load_dwordx4; dst must be wave-uniform).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t v, uint8_t *dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(v, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
 
 // One 256 x BN output tile: workgroup `pid` of the tiles of C[M][N] = A.B^T
 // (B, C and N already restricted to this tile width's column range).
@@ -106,16 +89,8 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
 
   // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  const int ntiles = tiles_m * tiles_n;
-  const int xcd = pid % kXcds, local = pid / kXcds;
-  const int q = ntiles / kXcds, rq = ntiles % kXcds;
-  const int logical = (xcd < rq) ? xcd * (q + 1) + local : rq * (q + 1) + (xcd - rq) * q + local;
-  const int per_group = kGroupM * tiles_n;
-  const int group = logical / per_group;
-  const int first_m = group * kGroupM;
-  const int gsz = min(tiles_m - first_m, kGroupM);
-  const int tm = first_m + (logical % per_group) % gsz;
-  const int tn = (logical % per_group) / gsz;
+  int tm, tn;
+  xcd_tile(pid, tiles_m, tiles_n, kGroupM, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   // ---- DMA side: waves 0 and 1 copy A rows 128w .. 128w+127, waves 2 and
@@ -374,7 +349,8 @@ __global__ void k_zero_c(void *C, int64_t M, int64_t N, int64_t ldc, int elem) {
   }
 }
 
-// Compute units of the current device (cached per device id).
+}  // namespace
+
 int device_cus() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -385,8 +361,6 @@ int device_cus() {
   cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
-
-}  // namespace
 
 hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_meta,
                        const uint8_t *b_codes, const uint8_t *b_scales, const float *b_meta, int64_t M,

@@ -8,6 +8,9 @@ namespace nvfp4 {
 
 constexpr int kQuantThreads = 256;
 
+// Compute units of the current device (cached per device id).
+int device_cus();
+
 // Enqueue meta reset, amax and encode for one quantization.  Arguments are
 // validated by the caller; x_dtype 0 = f32, 1 = bf16; rounding 0 = RNE,
 // 1 = SR; rht selects the fused Hadamard transform.
@@ -31,6 +34,14 @@ hipError_t launch_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_
                                 uint64_t seed1, uint64_t offset1, uint8_t *codes1, uint8_t *scales1, float *meta1,
                                 bool rht0, uint32_t sign_mask0, int rounding0, uint64_t seed0, uint64_t offset0,
                                 uint8_t *codes0, uint8_t *scales0, float *meta0, hipStream_t stream);
+
+// MXFP4 (32-element E2M1 blocks with E8M0 scales): quantize on axis 1 or 0,
+// and C = A . B^T on the block-scaled FP4 MFMA (K % 256 == 0).
+hipError_t launch_mx_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, uint8_t *codes,
+                              uint8_t *scales, hipStream_t stream);
+hipError_t launch_mx_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                          const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
+                          hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *meta, int64_t outer,
                              int64_t k, void *y, int y_dtype, hipStream_t stream);

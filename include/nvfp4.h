@@ -201,6 +201,45 @@ int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stre
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
                int64_t ldc, void *hip_stream);
 
+/*
+ * MXFP4 -- the microscaling format the pages set NVFP4 against ([P4]
+ * "Architektura NVFP4 kontra ograniczenia mikroskalowania": 32-element
+ * blocks sharing a power-of-two scale; no tensor-level scale).
+ *  codes  : u8 [outer][k/2], E2M1 codes two per byte (element 2j low
+ *           nibble), 16-byte aligned.
+ *  scales : u8 [outer][k/32], E8M0 exponents: the block scale is
+ *           2^(code - 127).
+ *  outer, k : k % 32 == 0.
+ * The value of element (o, kk) is e2m1(code) * 2^(scale - 127).
+ */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    int64_t outer;
+    int64_t k;
+} mxfp4_tensor;
+
+/*
+ * mxfp4_quantize -- x (row-major [rows][cols], x_dtype, 16-byte aligned)
+ * viewed on `axis` as in nvfp4_quantize.  Per 32-block along k: the scale is
+ * the smallest power of two 2^e with blockmax / 2^e <= 6 (e clamped to
+ * [-127, 127]; an all-zero block takes e = -127), so the block maximum is
+ * never clipped; each element is the nearest-even E2M1 code of x / 2^e.
+ * Enqueues one kernel.
+ */
+int mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis,
+                   mxfp4_tensor *out, void *hip_stream);
+
+/*
+ * mxfp4_gemm -- C[m][n] = sum_k (qA * 2^eA)[m][k] * (qB * 2^eB)[n][k] with
+ * FP32 accumulation on gfx950's block-scaled FP4 MFMA (the codes are not
+ * decoded).  a: M x K, b: N x K, both K-contiguous; K % 256 == 0
+ * (NVFP4_ERR_SHAPE otherwise).  c: row-major [M][ldc], f32 or bf16 (nearest
+ * even).  Accuracy as nvfp4_gemm: within 1e-5 * sum_k |a b|.  Deterministic.
+ */
+int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int c_dtype,
+               int64_t ldc, void *hip_stream);
+
 /* Human-readable name of a status code (static string). */
 const char *nvfp4_status_string(int status);
 

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:nvfp4|mxfp4)_[a-z_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -143,3 +143,28 @@ def test_amax_and_quantize_amax_argument_errors(L):
     assert call(FAKE, 1, 16, 32, 1, 0, 0, 0, 5, 0, FAKE, by(q), None) == -3   # rht
     assert call(FAKE, 1, 16, 32, 0, 0, 0, 0, 0, 0, FAKE, by(q), None) == -2   # axis-0 view is 32x16
     assert call(FAKE, 1, 16, 32, 1, 0, 0, 0, 0, 0, FAKE + 1, by(q), None) == -5
+
+
+def _mx(outer, k, codes=FAKE, scales=FAKE):
+    return nv._MXTensor(codes, scales, outer, k)
+
+
+@_no_gpu
+def test_mxfp4_argument_errors(L):
+    by = ctypes.byref
+    q = _mx(16, 64)
+    assert L.mxfp4_quantize(FAKE, 1, 16, 64, 1, None, None) == -1          # out NULL
+    assert L.mxfp4_quantize(FAKE, 7, 16, 64, 1, by(q), None) == -3         # dtype
+    assert L.mxfp4_quantize(FAKE, 1, 16, 64, 2, by(q), None) == -3         # axis
+    q48 = _mx(16, 48)
+    assert L.mxfp4_quantize(FAKE, 1, 16, 48, 1, by(q48), None) == -2       # K % 32
+    assert L.mxfp4_quantize(FAKE, 1, 16, 64, 0, by(q), None) == -2         # axis-0 view is 64x16
+    assert L.mxfp4_quantize(FAKE + 8, 1, 16, 64, 1, by(q), None) == -5     # x misaligned
+    assert L.mxfp4_quantize(FAKE, 1, 16, 64, 1, by(_mx(16, 64, codes=FAKE + 8)), None) == -5
+    a, b = _mx(8, 256), _mx(4, 256)
+    assert L.mxfp4_gemm(None, by(b), FAKE, 0, 4, None) == -1
+    assert L.mxfp4_gemm(by(a), by(_mx(4, 512)), FAKE, 0, 4, None) == -2    # K mismatch
+    assert L.mxfp4_gemm(by(_mx(8, 96)), by(_mx(4, 96)), FAKE, 0, 4, None) == -2   # K % 256
+    assert L.mxfp4_gemm(by(a), by(b), FAKE, 2, 4, None) == -3              # dtype
+    assert L.mxfp4_gemm(by(a), by(b), FAKE, 0, 3, None) == -2              # ldc < N
+    assert L.mxfp4_gemm(by(a), by(b), None, 0, 4, None) == -1              # c NULL

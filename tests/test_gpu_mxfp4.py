@@ -1,0 +1,78 @@
+"""GPU parity of the MXFP4 path against the CPU oracle: the quantizer
+bit-exact on codes and scales (axis 1 and 0, bf16 and f32, ragged shapes),
+the block-scaled FP4 MFMA GEMM within 1e-5 * sum|a*b| (bf16 outputs by the
+rounding interval), including tile tails and both tile widths.  Called
+through the C ABI."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=None)
+def _nv():
+    import gemm_amax_reduce_amd as nv
+    nv.lib()
+    return nv
+
+
+def _x(rows, cols, seed, dtype):
+    x = workloads.mixed_rows(rows, cols, seed)
+    x[: rows // 4] *= np.float32(1e-3)       # blocks of very different scale
+    return torch.from_numpy(x) if dtype == "f32" else workloads.to_bf16(x)
+
+
+@pytest.mark.parametrize("rows,cols,axis", [(32, 32, 1), (48, 96, 1), (272, 160, 1), (96, 64, 0), (320, 48, 0),
+                                            (512, 130, 0)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_matches_oracle(rows, cols, axis, dtype):
+    print(f"[mxfp4 quantize] {rows}x{cols} axis={axis} {dtype}", flush=True)
+    nv = _nv()
+    x = _x(rows, cols, 5, dtype)
+    q = nv.mxfp4_quantize(x.cuda(), axis=axis)
+    torch.cuda.synchronize()
+    ref = oracle.mxfp4_quantize(x, axis=axis)
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), ref.scales)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), ref.codes)
+
+
+def _gemm_case(m, n, k, out, seed=1):
+    nv = _nv()
+    xa, xb = _x(m, k, seed, "bf16"), _x(n, k, seed + 1, "bf16")
+    qa, qb = nv.mxfp4_quantize(xa.cuda()), nv.mxfp4_quantize(xb.cuda())
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    c = nv.mxfp4_gemm(qa, qb, dt)
+    torch.cuda.synchronize()
+    ra, rb = oracle.mxfp4_quantize(xa), oracle.mxfp4_quantize(xb)
+    cref, bound = oracle.mxfp4_gemm(ra, rb)
+    if out == "f32":
+        ok, worst = oracle.check_gemm_f32(c.cpu().numpy(), cref, bound, 1e-5)
+        assert ok, f"{m}x{n}x{k}: worst |err|/bound = {worst:.3e}"
+    else:
+        ok, nbad = oracle.check_gemm_bf16(c.double().cpu().numpy(), cref, bound, 1e-5)
+        assert ok, f"{m}x{n}x{k}: {nbad} bf16 outputs outside the tolerance interval"
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (200, 136, 512), (257, 129, 256), (1, 1, 256),
+                                   (384, 640, 1024), (64, 300, 768)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_matches_oracle(m, n, k, out):
+    print(f"[mxfp4 gemm] {m}x{n}x{k} {out}", flush=True)
+    _gemm_case(m, n, k, out)
+
+
+def test_gemm_k_rules():
+    nv = _nv()
+    a, b = nv.MXFP4Tensor.empty(8, 0), nv.MXFP4Tensor.empty(4, 0)
+    c = torch.full((8, 4), 5.0, device="cuda")
+    nv.mxfp4_gemm(a, b, out=c)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0)
+    with pytest.raises(nv.NVFP4Error, match="shape"):
+        nv.mxfp4_gemm(nv.MXFP4Tensor.empty(8, 96), nv.MXFP4Tensor.empty(4, 96))
