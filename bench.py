@@ -339,6 +339,55 @@ def main():
         bf16_ctx["gemm_time_ratio_bf16_over_nvfp4"] = round(tot_bf16 / nv_gemm_ms, 3)
         del W1t, X2t
 
+    # ------------------------------------------------ MXFP4 context ----
+    # The same linear-layer step in MXFP4 (32-element blocks, power-of-two
+    # scales) on the block-scaled FP4 MFMA: the format the pages set NVFP4
+    # against, measured on the same operands.  Context only.
+    mx_ctx = None
+    if not args.no_sweep:
+        mX1 = nv.MXFP4Tensor.empty(4096, 5120)
+        mW1 = nv.MXFP4Tensor.empty(5120, 5120)
+        mdY = nv.MXFP4Tensor.empty(8192, 20480)
+        mW2 = nv.MXFP4Tensor.empty(5120, 20480)
+        mX2 = nv.MXFP4Tensor.empty(5120, 8192)
+        mdYt = nv.MXFP4Tensor.empty(20480, 8192)
+        mx_ops = [
+            ("q fprop X", lambda: nv.mxfp4_quantize(X1, axis=1, out=mX1)),
+            ("q fprop W", lambda: nv.mxfp4_quantize(W1, axis=1, out=mW1)),
+            ("gemm fprop", lambda: nv.mxfp4_gemm(mX1, mW1, torch.bfloat16, out=Y)),
+            ("q dgrad dY", lambda: nv.mxfp4_quantize(dY, axis=1, out=mdY)),
+            ("q dgrad W (axis0)", lambda: nv.mxfp4_quantize(W2, axis=0, out=mW2)),
+            ("gemm dgrad", lambda: nv.mxfp4_gemm(mdY, mW2, torch.float32, out=dX)),
+            ("q wgrad X (axis0)", lambda: nv.mxfp4_quantize(X2, axis=0, out=mX2)),
+            ("q wgrad dY (axis0)", lambda: nv.mxfp4_quantize(dY, axis=0, out=mdYt)),
+            ("gemm wgrad", lambda: nv.mxfp4_gemm(mX2, mdYt, torch.float32, out=dW)),
+        ]
+        for _ in range(2):
+            for _, fn in mx_ops:
+                fn()
+        n_mx = 10
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(mx_ops) + 1)] for _ in range(n_mx)]
+        torch.cuda.synchronize()
+        for it in range(n_mx):
+            ev[it][0].record()
+            for i, (_, fn) in enumerate(mx_ops):
+                fn()
+                ev[it][i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([[ev[it][i].elapsed_time(ev[it][i + 1]) for i in range(len(mx_ops))] for it in range(n_mx)])
+        step_mx = float(np.median(per.sum(axis=1)))
+        mx_ctx = {"ms_per_step": round(step_mx, 4), "TFLOP/s": round(step_flops / (step_mx * 1e-3) / 1e12, 1),
+                  "breakdown": {}}
+        flops_of = {"gemm fprop": F.flops, "gemm dgrad": D.flops, "gemm wgrad": Wg.flops}
+        for i, (name, _) in enumerate(mx_ops):
+            ms = float(np.median(per[:, i]))
+            ent = {"ms": round(ms, 4)}
+            if name in flops_of:
+                ent["TFLOP/s"] = round(flops_of[name] / (ms * 1e-3) / 1e12, 1)
+                ent["frac_of_fp4_peak"] = round(flops_of[name] / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)
+            mx_ctx["breakdown"][name] = ent
+        del mX1, mW1, mdY, mW2, mX2, mdYt
+
     # ------------------------------------------------- CPU baseline ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -357,6 +406,7 @@ def main():
         "breakdown": breakdown,
         "quantize_sweep_32768x8192_bf16": sweep,
         "bf16_gemm_context": bf16_ctx,
+        "mxfp4_step_context": mx_ctx,
         "device": torch.cuda.get_device_name(0),
         "step_ms_event_median": round(float(np.median(step_ms)), 4),
     }
