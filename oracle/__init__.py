@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_rht16.restype = None
         L.oracle_quantize.argtypes = [vp, ctypes.c_int, c_i64, c_i64, ctypes.c_int,
                                       ctypes.c_int, c_u64, c_u64, ctypes.c_int, c_u32,
-                                      vp, vp, vp, vp]
+                                      vp, c_i64, vp, vp, vp]
         L.oracle_quantize.restype = ctypes.c_int
         L.oracle_dequantize.argtypes = [vp, vp, vp, c_i64, c_i64, ctypes.c_int, vp]
         L.oracle_dequantize.restype = ctypes.c_int
@@ -191,8 +191,10 @@ def _as_raw(x):
 
 
 def quantize(x, axis: int = 1, rounding: int = RNE, seed: int = 0, offset: int = 0,
-             rht: bool = False, sign_mask: int = 0, amax=None) -> Quantized:
-    """amax: None (computed, step 2) or a supplied tensor amax (float32)."""
+             rht: bool = False, sign_mask: int = 0, amax=None, outer0: int = 0) -> Quantized:
+    """amax: None (computed, step 2) or a supplied tensor amax (float32).
+    outer0: global index of x's first output row when x is a slice of a
+    larger tensor (shifts the SR element index only)."""
     a, dt = _as_raw(x)
     a = np.ascontiguousarray(a)
     rows, cols = a.shape
@@ -205,7 +207,7 @@ def quantize(x, axis: int = 1, rounding: int = RNE, seed: int = 0, offset: int =
     amax_in = None if amax is None else np.array([amax], dtype=np.float32)
     rc = lib().oracle_quantize(_ptr(a), dt, rows, cols, axis, rounding, seed, offset,
                                1 if rht else 0, sign_mask & 0xFFFF,
-                               None if amax_in is None else _ptr(amax_in),
+                               None if amax_in is None else _ptr(amax_in), int(outer0),
                                _ptr(codes), _ptr(scales), _ptr(meta))
     if rc != 0:
         raise ValueError(f"oracle_quantize failed: {rc}")

@@ -300,13 +300,19 @@ static void load_block(const void *x, int dtype, int64_t rows, int64_t cols,
  * Output layout: codes[o][K/2], scales[o][K/16], meta[2].
  * amax_in: NULL, or a supplied tensor amax that replaces step 2 (the scale
  * level the producer of x already knows; a smaller value than the true
- * maximum saturates: block scales at 448, codes at 6). */
+ * maximum saturates: block scales at 448, codes at 6).
+ * outer0: index of the first output row of x within a larger tensor (0 for
+ * a whole tensor).  It only shifts the SR element index, i = (outer0 + o)*K
+ * + k, so a slice of a tensor too large for this reference -- quantized
+ * with that tensor's amax supplied -- gets the codes of its rows in the
+ * whole tensor. */
 int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
                     int axis, int rounding, uint64_t seed, uint64_t offset,
                     int rht, uint32_t sign_mask, const float *amax_in,
+                    int64_t outer0,
                     uint8_t *codes, uint8_t *scales, float *meta)
 {
-    if (rows < 0 || cols < 0) return -2;
+    if (rows < 0 || cols < 0 || outer0 < 0) return -2;
     int64_t outer = axis ? rows : cols;
     int64_t K = axis ? cols : rows;
     if (K % 16 != 0) return -2;
@@ -360,7 +366,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
             for (int j = 0; j < 16; ++j) {
                 float v = y[j] * m;
                 if (rounding == OR_SR) {
-                    uint64_t i = (uint64_t)o * (uint64_t)K + (uint64_t)(16 * b + j);
+                    uint64_t i = (uint64_t)(outer0 + o) * (uint64_t)K + (uint64_t)(16 * b + j);
                     q[j] = oracle_e2m1_sr(v, oracle_sr_bits(seed, offset, i));
                 } else {
                     q[j] = oracle_e2m1_rne(v);

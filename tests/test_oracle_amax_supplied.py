@@ -50,3 +50,39 @@ def test_supplied_smaller_amax_saturates_at_it():
     assert q.g == 2.0 ** -10
     assert np.all(q.scales == 0x7E)          # saturated at 448
     np.testing.assert_array_equal(oracle.dequantize(q), np.clip(x, -2.625, 2.625))
+
+
+def test_slice_with_outer0_reproduces_its_rows():
+    """A slice of output rows, quantized with the whole tensor's amax and its
+    first row's global index, gets exactly the codes of those rows in the
+    whole tensor (both axes, SR): the SR element index is the output-layout
+    index o*K + k of the whole tensor."""
+    import workloads
+    x = workloads.normal(96, 160, seed=21)
+    full = oracle.quantize(x, axis=1, rounding=oracle.SR, seed=9, offset=3)
+    sub = oracle.quantize(x[40:72], axis=1, rounding=oracle.SR, seed=9, offset=3, amax=full.amax, outer0=40)
+    np.testing.assert_array_equal(sub.codes, full.codes[40:72])
+    np.testing.assert_array_equal(sub.scales, full.scales[40:72])
+    full0 = oracle.quantize(x, axis=0, rounding=oracle.SR, seed=9, offset=3)
+    sub0 = oracle.quantize(np.ascontiguousarray(x[:, 32:80]), axis=0, rounding=oracle.SR, seed=9, offset=3,
+                           amax=full0.amax, outer0=32)
+    np.testing.assert_array_equal(sub0.codes, full0.codes[32:80])
+    # without the offset the draws differ
+    sub_wrong = oracle.quantize(x[40:72], axis=1, rounding=oracle.SR, seed=9, offset=3, amax=full.amax)
+    assert not np.array_equal(sub_wrong.codes, full.codes[40:72])
+
+
+def test_outer0_shifts_the_counter_by_whole_rows():
+    """One row at a large global index: each code equals the SR primitive
+    applied with the Philox bits of element outer0*K + k."""
+    x = np.full((1, 32), 0.3, dtype=np.float32)
+    x[0, 0] = 6.0                       # amax 6: s_enc = 448, the block max maps to 6
+    outer0 = (1 << 33) + 5              # element indices above 2^35: the counter's second word is used
+    q = oracle.quantize(x, rounding=oracle.SR, seed=0x5EED, offset=7, amax=6.0, outer0=outer0)
+    # second block: m_b = s_enc / S_b in binary32
+    m = np.float32(448.0) / np.float32(oracle.e4m3_value(int(q.scales[0, 1])))
+    for k in range(16, 32):
+        v = np.float32(0.3) * m
+        want = oracle.e2m1_sr(float(v), oracle.sr_bits(0x5EED, 7, outer0 * 32 + k))
+        got = (q.codes[0, k // 2] >> (4 * (k & 1))) & 0xF
+        assert got == want, (k, got, want)
