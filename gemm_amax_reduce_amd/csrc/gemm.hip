@@ -155,6 +155,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   }
   u32x4 codes[2][NF];      // [stage parity][fragment]: this lane's 32 codes
   uint32_t sraw[NF];       // their two E4M3 block scales
+  uint32_t keep = 0;       // which of those two scales lie inside K
   half2_t spair[NF];       // ... as an f16 pair
   half8_t opnd[2][NF];     // [K step parity][fragment]: decoded MFMA operands
   float16_t acc[4][NB];
@@ -168,6 +169,9 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   // Codes and scales of stage sp of group g (LDS buffer gb) into codes[cb].
   // The scales of 16-blocks at or past K are zeroed, which zeroes those
   // products whatever codes the DMA left there (every E2M1 value is finite).
+  // The mask is applied where the scales are converted, a few K steps
+  // later: using the loaded values here would make the wave wait for the
+  // LDS reads right after issuing them.
   const int k32 = (int)K;    // K < 2^25 (checked by the launcher)
   auto read_stage = [&](int cb, const uint8_t *gb, int g, int sp) {
     const int c = 2 * sp + h;
@@ -187,13 +191,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
       }
     }
     const int kc = kGroupK * g + 32 * c;
-    const uint32_t keep = (kc < k32 ? 0x00FFu : 0u) | (kc + 16 < k32 ? 0xFF00u : 0u);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) sraw[f] &= keep;
+    keep = (kc < k32 ? 0x00FFu : 0u) | (kc + 16 < k32 ? 0xFF00u : 0u);
   };
   auto scale_pairs = [&]() {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) spair[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[f], 1.0f, false);
+    for (int f = 0; f < NF; ++f) spair[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[f] & keep, 1.0f, false);
   };
   // Half `part` (bytes 2part, 2part+1 = 4 codes) of word ks of fragment f:
   // K step ks lies in 16-block ks/2 of the chunk.
@@ -393,7 +395,9 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
     const double cost = (double)rounds(tm * t1) + 0.55 * (double)rounds(tm * rest);
     if (cost < best - 1e-9) { best = cost; best_n1 = n1; }
   }
-  const int64_t n_big = tm * (best_n1 / 256), n_small = tm * ((N - best_n1 + 127) / 128);
+  // best_n1 is a multiple of 256 or N itself (no split: the last tile
+  // column may be ragged, so round up)
+  const int64_t n_big = tm * ((best_n1 + 255) / 256), n_small = tm * ((N - best_n1 + 127) / 128);
   if (n_big + n_small > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(n_big + n_small));
   // Scale rows go through the DMA only when they are whole dwords (K % 64

@@ -361,7 +361,9 @@ hipError_t launch_mx_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const
     const double cost = (double)rounds(tm * t1) + 0.55 * (double)rounds(tm * rest);
     if (cost < best - 1e-9) { best = cost; best_n1 = n1; }
   }
-  const int64_t n_big = tm * (best_n1 / 256), n_small = tm * ((N - best_n1 + 127) / 128);
+  // best_n1 is a multiple of 256 or N itself (no split: the last tile
+  // column may be ragged, so round up)
+  const int64_t n_big = tm * ((best_n1 + 255) / 256), n_small = tm * ((N - best_n1 + 127) / 128);
   if (n_big + n_small > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(n_big + n_small));
   if (c_dtype == 0)

@@ -78,8 +78,10 @@ def test_tiny_config():
     _check(c, ra, rb, "f32", label="tiny")
 
 
+# (64, 40000, 64): 157 tile columns in one row of tiles, the launcher keeps
+# every column at 256 wide (no 128-wide remainder) and the last one is ragged
 @pytest.mark.parametrize("m,n,k", [(128, 128, 128), (200, 136, 272), (257, 129, 16), (64, 300, 528),
-                                   (1, 1, 16), (3, 517, 48), (384, 256, 1024)])
+                                   (1, 1, 16), (3, 517, 48), (384, 256, 1024), (64, 40000, 64)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_ragged_shapes(m, n, k, out):
     print(f"[gemm] {m}x{n}x{k} {out}", flush=True)

@@ -60,7 +60,7 @@ def _gemm_case(m, n, k, out, seed=1):
 
 
 @pytest.mark.parametrize("m,n,k", [(256, 256, 256), (200, 136, 512), (257, 129, 256), (1, 1, 256),
-                                   (384, 640, 1024), (64, 300, 768)])
+                                   (384, 640, 1024), (64, 300, 768), (64, 40000, 256)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_matches_oracle(m, n, k, out):
     print(f"[mxfp4 gemm] {m}x{n}x{k} {out}", flush=True)
