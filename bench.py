@@ -67,7 +67,7 @@ def log(msg):
 # region).  The profile records a hash of the kernel sources; when they have
 # changed since, the traffic is reported as null.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_f32_dgrad_wgrad_traffic.json")
-GEMM_SOURCES = [os.path.join(ROOT, "gemm_amax_reduce_amd", "csrc", f) for f in ("gemm.hip", "nvfp4_device.h")]
+GEMM_SOURCES = [os.path.join(ROOT, "gemm_amax_reduce_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h", "nvfp4_device.h")]
 DOMINANT = "k_gemm_nvfp4<false, true>"   # f32 output, scales by DMA (K % 64 == 0)
 CALIB_BYTES = 256 << 20
 
