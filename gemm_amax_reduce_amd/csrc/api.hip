@@ -4,9 +4,29 @@
 #include "nvfp4.h"
 #include "nvfp4_kernels.h"
 
+#include <stdint.h>
+
 namespace {
 
+// Size limits of the launch geometry (each documented in nvfp4.h).
+// Quantization down the columns (axis 0) puts 16-row blocks on the grid's
+// y dimension (at most 65535): 4 blocks per y step for NVFP4, 8 x 32 rows
+// for MXFP4.
+constexpr int64_t kMaxRowsAxis0 = 65535LL * 4 * 16;       // 4 194 240
+constexpr int64_t kMaxRowsAxis0Mx = 65535LL * 8 * 32;     // 16 776 960
+// The GEMMs address 128 operand rows of K/2 code bytes with 32-bit buffer
+// offsets below 2^31, and launch at most INT32_MAX workgroups (tiles of
+// 256 x 128 or larger).
+constexpr int64_t kMaxGemmK = (1LL << 25) - 16;
+
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
+  if (K > kMaxGemmK) return false;
+  // ceil(M/256) * ceil(N/128) <= INT32_MAX, without overflow
+  const int64_t tm = M / 256 + (M % 256 != 0), tn = N / 128 + (N % 128 != 0);
+  return tn == 0 || tm <= INT32_MAX / tn;
+}
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
@@ -30,6 +50,7 @@ int quantize_common(const void *x, int x_dtype, int64_t rows, int64_t cols, int 
   const int64_t k = axis ? cols : rows;
   if (k % 16 != 0) return NVFP4_ERR_SHAPE;
   if (out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
+  if (axis == 0 && rows > kMaxRowsAxis0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
   int st = check_tensor(out);
   if (st != NVFP4_OK) return st;
@@ -61,6 +82,7 @@ int nvfp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis,
   if (rht != 0 && rht != 1) return NVFP4_ERR_ENUM;
   if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
   if ((axis ? cols : rows) % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (axis == 0 && rows > kMaxRowsAxis0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_amax(x, x_dtype, rows, cols, axis, rht != 0, sign_mask, amax,
@@ -80,6 +102,7 @@ int nvfp4_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   const int64_t k = axis ? cols : rows;
   if (k % 16 != 0) return NVFP4_ERR_SHAPE;
   if (out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
+  if (axis == 0 && rows > kMaxRowsAxis0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
   int st = check_tensor(out);
   if (st != NVFP4_OK) return st;
@@ -99,6 +122,7 @@ int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   if (rht0 != 0 && rht0 != 1) return NVFP4_ERR_ENUM;
   if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (out1->outer != rows || out1->k != cols || out0->outer != cols || out0->k != rows) return NVFP4_ERR_SHAPE;
+  if (rows > kMaxRowsAxis0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
   int st = check_tensor(out1);
   if (st != NVFP4_OK) return st;
@@ -120,6 +144,7 @@ int mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int a
   if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
   const int64_t outer = axis ? rows : cols, k = axis ? cols : rows;
   if (k % 32 != 0 || out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
+  if (axis == 0 && rows > kMaxRowsAxis0Mx) return NVFP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (!x || !out->codes || !out->scales)) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(out->codes, 16)) return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_mx_quantize(x, x_dtype, rows, cols, axis, out->codes, out->scales,
@@ -131,7 +156,7 @@ int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int c_dtyp
   if (a->outer < 0 || b->outer < 0 || a->k < 0 || a->k != b->k || a->k % 256 != 0) return NVFP4_ERR_SHAPE;
   if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
   const int64_t M = a->outer, N = b->outer;
-  if (ldc < N) return NVFP4_ERR_SHAPE;
+  if (ldc < N || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
   if (M > 0 && N > 0 && (!c || (a->k > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
     return NVFP4_ERR_NULL;
   if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
@@ -157,7 +182,7 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
   if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
   if (a->k != b->k) return NVFP4_ERR_SHAPE;
   const int64_t M = a->outer, N = b->outer;
-  if (ldc < N || ldc < 0) return NVFP4_ERR_SHAPE;
+  if (ldc < N || ldc < 0 || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
   if (M > 0 && N > 0 && !c) return NVFP4_ERR_NULL;
   if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_gemm(a->codes, a->scales, a->meta, b->codes, b->scales, b->meta, M, N, a->k, c,

@@ -27,6 +27,10 @@
  *  - Argument errors are reported synchronously, before anything is
  *    launched.  NVFP4_ERR_HIP reports a failed launch.
  *  - Sizes are int64_t and may be 0 (empty tensors are valid, see below).
+ *    Limits of the launch geometry (NVFP4_ERR_SHAPE beyond them):
+ *    quantization down the columns (axis 0, and the dual call) takes
+ *    rows <= 4 194 240 (MXFP4: 16 776 960); the GEMMs take K <= 2^25 - 16
+ *    and ceil(M/256) * ceil(N/128) <= INT32_MAX.
  *  - Element types: NVFP4_F32 (binary32) or NVFP4_BF16 (bfloat16).
  *  - Thread safety: stateless; concurrent calls on different outputs are
  *    fine.  The calls keep no scratch memory between launches.
@@ -43,7 +47,8 @@ extern "C" {
 typedef enum {
     NVFP4_OK = 0,
     NVFP4_ERR_NULL = -1,   /* a required pointer is NULL                      */
-    NVFP4_ERR_SHAPE = -2,  /* negative size, K % 16 != 0, mismatched shapes   */
+    NVFP4_ERR_SHAPE = -2,  /* negative size, K % 16 != 0, mismatched shapes,
+                              size beyond a documented limit                */
     NVFP4_ERR_ENUM = -3,   /* unknown dtype / rounding / axis value           */
     NVFP4_ERR_HIP = -4,    /* a HIP launch failed                             */
     NVFP4_ERR_ALIGN = -5   /* a pointer or leading dimension is misaligned    */

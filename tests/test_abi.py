@@ -168,3 +168,26 @@ def test_mxfp4_argument_errors(L):
     assert L.mxfp4_gemm(by(a), by(b), FAKE, 2, 4, None) == -3              # dtype
     assert L.mxfp4_gemm(by(a), by(b), FAKE, 0, 3, None) == -2              # ldc < N
     assert L.mxfp4_gemm(by(a), by(b), None, 0, 4, None) == -1              # c NULL
+
+
+@_no_gpu
+def test_size_limits_are_shape_errors(L):
+    """Sizes beyond the documented launch-geometry limits are refused before
+    anything is launched (NVFP4_ERR_SHAPE)."""
+    by = ctypes.byref
+    rows = 4194240 + 16                                  # axis 0: rows <= 4 194 240
+    q0 = _t(16, rows)
+    assert L.nvfp4_quantize(FAKE, 1, rows, 16, 0, 0, 0, 0, by(q0), None) == -2
+    assert L.nvfp4_rht_quantize(FAKE, 1, rows, 16, 0, 0, 0, 0, 0, by(q0), None) == -2
+    assert L.nvfp4_amax(FAKE, 1, rows, 16, 0, 0, 0, FAKE, None) == -2
+    assert L.nvfp4_quantize_amax(FAKE, 1, rows, 16, 0, 0, 0, 0, 0, 0, FAKE, by(q0), None) == -2
+    q1 = _t(rows, 16)
+    assert L.nvfp4_quantize_dual(FAKE, 1, rows, 16, 0, 0, 0, by(q1), 0, 0, 0, 0, 0,
+                                 by(_t(16, rows, meta=FAKE + 64)), None) == -2
+    mrows = 16776960 + 32                                # MXFP4 axis 0: rows <= 16 776 960
+    assert L.mxfp4_quantize(FAKE, 1, mrows, 64, 0, by(_mx(64, mrows)), None) == -2
+    k = 1 << 25                                          # GEMM: K <= 2^25 - 16
+    assert L.nvfp4_gemm(by(_t(4, k)), by(_t(4, k)), FAKE, 0, 4, None) == -2
+    assert L.mxfp4_gemm(by(_mx(4, k)), by(_mx(4, k)), FAKE, 0, 4, None) == -2
+    big = 1 << 40                                        # more tiles than a grid holds
+    assert L.nvfp4_gemm(by(_t(big, 16)), by(_t(big, 16)), FAKE, 0, big, None) == -2
