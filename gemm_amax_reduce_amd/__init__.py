@@ -89,14 +89,49 @@ def _check(rc: int, what: str):
         raise NVFP4Error(f"{what} failed: {msg} ({rc})")
 
 
-def _stream_handle(stream) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream_handle(stream, device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return int(s.cuda_stream)
 
 
 def _require_device(t: torch.Tensor, name: str):
     if not t.is_cuda:
         raise NVFP4Error(f"{name} must be a GPU tensor (no CPU path exists)")
+
+
+def _require_buffer(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int, device: torch.device):
+    """A caller-supplied device buffer the kernels write or read whole: the
+    C ABI cannot see its size, so it is checked here."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise NVFP4Error(f"{name} must be a GPU tensor on {device}")
+    if t.dtype != dtype:
+        raise NVFP4Error(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous() or t.numel() < numel:
+        raise NVFP4Error(f"{name} must be contiguous with at least {numel} elements")
+
+
+def _out_code(dtype) -> int:
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    raise NVFP4Error(f"unsupported output dtype {dtype} (float32 or bfloat16)")
+
+
+def _require_matrix_out(out: torch.Tensor, rows: int, cols: int, dtype, device: torch.device) -> int:
+    """Check a caller-supplied [rows][cols] output view (row stride >= cols)
+    and return its leading dimension."""
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.device != device:
+        raise NVFP4Error(f"out must be a GPU tensor on {device}")
+    if out.dtype != dtype:
+        raise NVFP4Error(f"out has dtype {out.dtype}, expected {dtype}")
+    if out.dim() != 2 or tuple(out.shape) != (rows, cols):
+        raise NVFP4Error(f"out must have shape ({rows}, {cols}), got {tuple(out.shape)}")
+    if cols > 1 and out.stride(1) != 1:
+        raise NVFP4Error("out must be row-major (unit column stride)")
+    if rows > 1 and out.stride(0) < cols:
+        raise NVFP4Error("out rows overlap (row stride < columns)")
+    return out.stride(0) if rows > 1 else max(cols, 1)
 
 
 class NVFP4Tensor:
@@ -116,7 +151,17 @@ class NVFP4Tensor:
         meta = torch.empty(2, dtype=torch.float32, device=device)
         return cls(codes, scales, meta, outer, k)
 
+    @property
+    def device(self) -> torch.device:
+        return self.codes.device
+
     def _c(self) -> _CTensor:
+        if self.outer < 0 or self.k < 0 or self.k % 16:
+            raise NVFP4Error(f"invalid NVFP4 shape ({self.outer}, {self.k})")
+        dev = self.codes.device
+        _require_buffer(self.codes, "codes", torch.uint8, self.outer * (self.k // 2), dev)
+        _require_buffer(self.scales, "scales", torch.uint8, self.outer * (self.k // 16), dev)
+        _require_buffer(self.meta, "meta", torch.float32, 2, dev)
         return _CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.meta.data_ptr(), self.outer, self.k)
 
     @property
@@ -138,6 +183,11 @@ def _rounding_code(r) -> int:
     return int(r)
 
 
+def _same_device(q, x: torch.Tensor):
+    if q.device != x.device:
+        raise NVFP4Error(f"output on {q.device}, input on {x.device}")
+
+
 def _quantize(x, axis, rounding, seed, offset, rht, sign_mask, out, stream):
     _require_device(x, "x")
     if x.dim() != 2 or not x.is_contiguous():
@@ -146,13 +196,16 @@ def _quantize(x, axis, rounding, seed, offset, rht, sign_mask, out, stream):
     outer, k = (rows, cols) if axis == 1 else (cols, rows)
     if out is None:
         out = NVFP4Tensor.empty(outer, k, device=x.device)
+    _same_device(out, x)
     ct = out._c()
-    if rht:
-        rc = lib().nvfp4_rht_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding),
-                                      seed, offset, sign_mask & 0xFFFF, ctypes.byref(ct), _stream_handle(stream))
-    else:
-        rc = lib().nvfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding),
-                                  seed, offset, ctypes.byref(ct), _stream_handle(stream))
+    with torch.cuda.device(x.device):
+        if rht:
+            rc = lib().nvfp4_rht_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding),
+                                          seed, offset, sign_mask & 0xFFFF, ctypes.byref(ct),
+                                          _stream_handle(stream, x.device))
+        else:
+            rc = lib().nvfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding),
+                                      seed, offset, ctypes.byref(ct), _stream_handle(stream, x.device))
     _check(rc, "nvfp4_rht_quantize" if rht else "nvfp4_quantize")
     return out
 
@@ -177,9 +230,11 @@ def nvfp4_amax(x: torch.Tensor, axis: int = 1, rht: bool = False, sign_mask: int
         raise NVFP4Error("x must be a contiguous 2-D tensor")
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _require_buffer(out, "out", torch.float32, 1, x.device)
     rows, cols = x.shape
-    _check(lib().nvfp4_amax(x.data_ptr(), _dtype_code(x), rows, cols, axis, int(bool(rht)), sign_mask & 0xFFFF,
-                            out.data_ptr(), _stream_handle(stream)), "nvfp4_amax")
+    with torch.cuda.device(x.device):
+        _check(lib().nvfp4_amax(x.data_ptr(), _dtype_code(x), rows, cols, axis, int(bool(rht)), sign_mask & 0xFFFF,
+                                out.data_ptr(), _stream_handle(stream, x.device)), "nvfp4_amax")
     return out
 
 
@@ -191,16 +246,17 @@ def nvfp4_quantize_amax(x: torch.Tensor, amax: torch.Tensor, axis: int = 1, roun
     _require_device(amax, "amax")
     if x.dim() != 2 or not x.is_contiguous():
         raise NVFP4Error("x must be a contiguous 2-D tensor")
-    if amax.dtype != torch.float32 or amax.numel() < 1:
-        raise NVFP4Error("amax must be a float32 tensor with at least one element")
+    _require_buffer(amax, "amax", torch.float32, 1, x.device)
     rows, cols = x.shape
     outer, k = (rows, cols) if axis == 1 else (cols, rows)
     if out is None:
         out = NVFP4Tensor.empty(outer, k, device=x.device)
+    _same_device(out, x)
     ct = out._c()
-    _check(lib().nvfp4_quantize_amax(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding), seed,
-                                     offset, int(bool(rht)), sign_mask & 0xFFFF, amax.data_ptr(), ctypes.byref(ct),
-                                     _stream_handle(stream)), "nvfp4_quantize_amax")
+    with torch.cuda.device(x.device):
+        _check(lib().nvfp4_quantize_amax(x.data_ptr(), _dtype_code(x), rows, cols, axis, _rounding_code(rounding),
+                                         seed, offset, int(bool(rht)), sign_mask & 0xFFFF, amax.data_ptr(),
+                                         ctypes.byref(ct), _stream_handle(stream, x.device)), "nvfp4_quantize_amax")
     return out
 
 
@@ -218,11 +274,14 @@ def nvfp4_quantize_dual(x: torch.Tensor, rounding1="rne", seed1: int = 0, offset
         out1 = NVFP4Tensor.empty(rows, cols, device=x.device)
     if out0 is None:
         out0 = NVFP4Tensor.empty(cols, rows, device=x.device)
+    _same_device(out1, x)
+    _same_device(out0, x)
     c1, c0 = out1._c(), out0._c()
-    rc = lib().nvfp4_quantize_dual(x.data_ptr(), _dtype_code(x), rows, cols, _rounding_code(rounding1), seed1,
-                                   offset1, ctypes.byref(c1), int(bool(rht0)), sign_mask0 & 0xFFFF,
-                                   _rounding_code(rounding0), seed0, offset0, ctypes.byref(c0),
-                                   _stream_handle(stream))
+    with torch.cuda.device(x.device):
+        rc = lib().nvfp4_quantize_dual(x.data_ptr(), _dtype_code(x), rows, cols, _rounding_code(rounding1), seed1,
+                                       offset1, ctypes.byref(c1), int(bool(rht0)), sign_mask0 & 0xFFFF,
+                                       _rounding_code(rounding0), seed0, offset0, ctypes.byref(c0),
+                                       _stream_handle(stream, x.device))
     _check(rc, "nvfp4_quantize_dual")
     return out1, out0
 
@@ -230,27 +289,32 @@ def nvfp4_quantize_dual(x: torch.Tensor, rounding1="rne", seed1: int = 0, offset
 def nvfp4_dequantize(q: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None,
                      stream=None) -> torch.Tensor:
     """Decode to f32/bf16 in the quantized [outer][k] layout."""
-    code = F32 if dtype == torch.float32 else BF16
+    code = _out_code(dtype)
+    dev = q.device
     if out is None:
-        out = torch.empty((q.outer, q.k), dtype=dtype, device=q.codes.device)
+        out = torch.empty((q.outer, q.k), dtype=dtype, device=dev)
+    _require_buffer(out, "out", dtype, q.outer * q.k, dev)
     ct = q._c()
-    _check(lib().nvfp4_dequantize(ctypes.byref(ct), out.data_ptr(), code, _stream_handle(stream)),
-           "nvfp4_dequantize")
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_dequantize(ctypes.byref(ct), out.data_ptr(), code, _stream_handle(stream, dev)),
+               "nvfp4_dequantize")
     return out
 
 
 def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
     """C = A . B^T for A [M, K] and B [N, K] NVFP4 tensors, f32 accumulation."""
-    code = F32 if out_dtype == torch.float32 else BF16
+    code = _out_code(out_dtype)
+    dev = a.device
+    if b.device != dev:
+        raise NVFP4Error(f"operands on {a.device} and {b.device}")
     if out is None:
-        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=a.codes.device)
-    if out.dim() != 2 or out.stride(1) != 1:
-        raise NVFP4Error("out must be a row-major 2-D tensor")
-    ldc = out.stride(0) if out.shape[0] > 1 else max(out.shape[1], 1)
+        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=dev)
+    ldc = _require_matrix_out(out, a.outer, b.outer, out_dtype, dev)
     ca, cb = a._c(), b._c()
-    _check(lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
-                            _stream_handle(stream)), "nvfp4_gemm")
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
+                                _stream_handle(stream, dev)), "nvfp4_gemm")
     return out
 
 
@@ -267,7 +331,16 @@ class MXFP4Tensor:
         return cls(torch.empty((outer, k // 2), dtype=torch.uint8, device=device),
                    torch.empty((outer, k // 32), dtype=torch.uint8, device=device), outer, k)
 
+    @property
+    def device(self) -> torch.device:
+        return self.codes.device
+
     def _c(self) -> _MXTensor:
+        if self.outer < 0 or self.k < 0 or self.k % 32:
+            raise NVFP4Error(f"invalid MXFP4 shape ({self.outer}, {self.k})")
+        dev = self.codes.device
+        _require_buffer(self.codes, "codes", torch.uint8, self.outer * (self.k // 2), dev)
+        _require_buffer(self.scales, "scales", torch.uint8, self.outer * (self.k // 32), dev)
         return _MXTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.outer, self.k)
 
 
@@ -280,23 +353,27 @@ def mxfp4_quantize(x: torch.Tensor, axis: int = 1, out: MXFP4Tensor | None = Non
     outer, k = (rows, cols) if axis == 1 else (cols, rows)
     if out is None:
         out = MXFP4Tensor.empty(outer, k, device=x.device)
+    _same_device(out, x)
     ct = out._c()
-    _check(lib().mxfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, ctypes.byref(ct),
-                                _stream_handle(stream)), "mxfp4_quantize")
+    with torch.cuda.device(x.device):
+        _check(lib().mxfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, ctypes.byref(ct),
+                                    _stream_handle(stream, x.device)), "mxfp4_quantize")
     return out
 
 
 def mxfp4_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
     """C = A . B^T for MXFP4 A [M, K] and B [N, K] (K % 256 == 0), f32 accumulation."""
-    code = F32 if out_dtype == torch.float32 else BF16
+    code = _out_code(out_dtype)
+    dev = a.device
+    if b.device != dev:
+        raise NVFP4Error(f"operands on {a.device} and {b.device}")
     if out is None:
-        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=a.codes.device)
-    if out.dim() != 2 or out.stride(1) != 1:
-        raise NVFP4Error("out must be a row-major 2-D tensor")
-    ldc = out.stride(0) if out.shape[0] > 1 else max(out.shape[1], 1)
+        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=dev)
+    ldc = _require_matrix_out(out, a.outer, b.outer, out_dtype, dev)
     ca, cb = a._c(), b._c()
-    _check(lib().mxfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc, _stream_handle(stream)),
-           "mxfp4_gemm")
+    with torch.cuda.device(dev):
+        _check(lib().mxfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
+                                _stream_handle(stream, dev)), "mxfp4_gemm")
     return out
 

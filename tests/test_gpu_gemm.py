@@ -179,3 +179,27 @@ def test_full_workload_end_to_end(name):
         # the f32 result of the same launch configuration, checked strictly
         c32 = _gemm(qa, qb, "f32")
         _check(c32, ra, rb, "f32", rows=rows, label=f"{name} f32 rows")
+
+
+def test_binding_rejects_bad_buffers():
+    """The C ABI cannot see buffer sizes, so the binding checks every
+    caller-supplied buffer before the call (nothing is launched)."""
+    nv = _nv()
+    qa, qb = _upload(_rand_q(64, 64, 5)), _upload(_rand_q(32, 64, 6))
+    with pytest.raises(nv.NVFP4Error, match="shape"):
+        nv.nvfp4_gemm(qa, qb, out=torch.empty((64, 31), device="cuda"))
+    with pytest.raises(nv.NVFP4Error, match="dtype"):
+        nv.nvfp4_gemm(qa, qb, out=torch.empty((64, 32), dtype=torch.float16, device="cuda"))
+    with pytest.raises(nv.NVFP4Error, match="output dtype"):
+        nv.nvfp4_gemm(qa, qb, torch.float16)
+    with pytest.raises(nv.NVFP4Error, match="overlap"):
+        nv.nvfp4_gemm(qa, qb, out=torch.empty((64, 64), device="cuda").as_strided((64, 32), (16, 1)))
+    short = nv.NVFP4Tensor(qa.codes[:32], qa.scales, qa.meta, 64, 64)
+    with pytest.raises(nv.NVFP4Error, match="codes"):
+        nv.nvfp4_gemm(short, qb)
+    with pytest.raises(nv.NVFP4Error, match="codes"):
+        nv.nvfp4_quantize(torch.zeros((64, 64), device="cuda"), out=short)
+    with pytest.raises(nv.NVFP4Error, match="out"):
+        nv.nvfp4_dequantize(qa, out=torch.empty((64, 63), device="cuda"))
+    with pytest.raises(nv.NVFP4Error, match="meta"):
+        nv.nvfp4_gemm(nv.NVFP4Tensor(qa.codes, qa.scales, qa.meta.double(), 64, 64), qb)
