@@ -12,9 +12,11 @@ resident in HBM before timing starts:
 dY's two quantizations run as one dual-layout call (one amax read for both).
 value = GEMM FLOP of the step / step time (quantization included), TFLOP/s.
 Also reported: quantizer GB/s per operand and on the 32768x8192 sweep tensor
-(RNE/SR x RHT off/on), per-GEMM TFLOP/s, the roofline of the dominant kernel
-(the f32-output GEMM that serves dgrad and wgrad), and the CPU oracle timed
-on a bounded sample of the same step.
+(RNE/SR x RHT off/on), the fprop operands' quantization warm and after a
+512 MiB cache flush, per-GEMM TFLOP/s, the roofline of the dominant kernel
+(the f32-output GEMM that serves dgrad and wgrad), the same products in bf16
+and the same step in MXFP4 as context, and the CPU oracle timed on a bounded
+sample of the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -308,6 +310,33 @@ def main():
                         "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4)}
         del T, qT, qTt
 
+    # ------------------------------- fprop operands, warm and cold ----
+    # The fprop operands (40-50 MB) fit the 256 MB MALL, so in the step the
+    # encode pass re-reads them partly from cache.  Each is timed again
+    # right after a 512 MiB write that evicts them (the write itself outside
+    # the timed region).
+    fprop_cache = None
+    if not args.no_sweep:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fprop_cache = {}
+        for name, x, out in (("X 4096x5120 bf16", X1, qX1), ("W 5120x5120 bf16", W1, qW1)):
+            b = qbytes(x.numel(), x.element_size())
+            warm, cold = [], []
+            for _ in range(7):
+                for label, prep in (("warm", lambda: nv.nvfp4_quantize(x, axis=1, out=out)),
+                                    ("cold", lambda: flush.fill_(1))):
+                    prep()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    nv.nvfp4_quantize(x, axis=1, out=out)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    (warm if label == "warm" else cold).append(e0.elapsed_time(e1))
+            w, c = sorted(warm)[3], sorted(cold)[3]
+            fprop_cache[name] = {"warm_ms": round(w, 4), "warm_GB/s": round(b / (w * 1e-3) / 1e9, 1),
+                                 "after_flush_ms": round(c, 4), "after_flush_GB/s": round(b / (c * 1e-3) / 1e9, 1)}
+        del flush
+
     # ------------------------------------------- BF16 GEMM context ----
     # The same three products in bf16 through torch.matmul (hipBLASLt), to
     # state the 4-bit path's speed against a 16-bit one as a measured ratio.
@@ -405,6 +434,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": breakdown,
         "quantize_sweep_32768x8192_bf16": sweep,
+        "fprop_quantize_warm_vs_flushed": fprop_cache,
         "bf16_gemm_context": bf16_ctx,
         "mxfp4_step_context": mx_ctx,
         "device": torch.cuda.get_device_name(0),
