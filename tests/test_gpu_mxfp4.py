@@ -76,3 +76,39 @@ def test_gemm_k_rules():
     assert torch.all(c == 0)
     with pytest.raises(nv.NVFP4Error, match="shape"):
         nv.mxfp4_gemm(nv.MXFP4Tensor.empty(8, 96), nv.MXFP4Tensor.empty(4, 96))
+
+
+@pytest.mark.parametrize("name", ["fprop", "dgrad", "wgrad"])
+def test_full_workload_step(name):
+    """The MXFP4 step at the full layer shapes, as the benchmark runs it:
+    both operands quantized on the GPU (bit-exact against the oracle on the
+    whole tensors, along the layer's axes), then the GEMM checked on 128+
+    sampled rows and columns (every tile position of the sampled lines)."""
+    nv = _nv()
+    g = workloads.GEMMS[name]
+    m, n, k = g.mnk
+    print(f"[mxfp4] full {name} {g.mnk}", flush=True)
+    qs = []
+    for op in (g.a, g.b):
+        x = op.generate()
+        ref = oracle.mxfp4_quantize(x, axis=op.axis)
+        q = nv.mxfp4_quantize(x.cuda(), axis=op.axis)
+        torch.cuda.synchronize()
+        assert torch.equal(q.scales.cpu(), torch.from_numpy(ref.scales)), f"{name} scales"
+        assert torch.equal(q.codes.cpu(), torch.from_numpy(ref.codes)), f"{name} codes"
+        qs.append((q, ref))
+    (qa, ra), (qb, rb) = qs
+    dt = torch.float32 if g.out == "f32" else torch.bfloat16
+    c = nv.mxfp4_gemm(qa, qb, dt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 128, replace=False)]))
+    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 128, replace=False)]))
+    cref, bound = oracle.mxfp4_gemm(ra, rb, rows, cols)
+    got = c[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")].double().cpu().numpy()
+    if g.out == "f32":
+        ok, worst = oracle.check_gemm_f32(got, cref, bound, 1e-5)
+        assert ok, f"{name}: worst |err|/bound = {worst:.3e}"
+    else:
+        ok, nbad = oracle.check_gemm_bf16(got, cref, bound, 1e-5)
+        assert ok, f"{name}: {nbad} bf16 outputs outside the tolerance interval"
