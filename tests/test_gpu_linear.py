@@ -86,3 +86,37 @@ def test_successive_calls_draw_fresh_offsets():
         grads.append(x.grad.clone())
     torch.cuda.synchronize()
     assert not torch.equal(grads[0], grads[1])     # stochastic rounding differs between steps
+
+
+def test_full_layer_shape_bf16():
+    """The layer at the benchmark's large shape (8192 tokens, 5120 -> 20480,
+    bf16): y, dx and dW on sampled rows and columns against the oracle's
+    quantizations of the same tensors (x N(0,1), dy Laplace(1e-3))."""
+    import gemm_amax_reduce_amd.linear as L
+    tokens, fin, fout = 8192, 5120, 20480
+    print(f"[linear] {tokens}x{fin} -> {fout} bf16", flush=True)
+    torch.manual_seed(1)
+    layer = L.NVFP4Linear(fin, fout, seed=0x5EED, sign_mask=MASK, device="cuda", dtype=torch.bfloat16)
+    x = workloads.to_bf16(workloads.normal(tokens, fin, 31)).cuda().requires_grad_(True)
+    dy = workloads.to_bf16(workloads.laplace(tokens, fout, 32, 1e-3)).cuda()
+    y = layer(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    xc, wc, dyc = x.detach().cpu(), layer.weight.detach().cpu(), dy.cpu()
+    rng = np.random.default_rng(33)
+
+    def pick(n):
+        return np.unique(np.concatenate([[0, n - 1], rng.choice(n, 64, replace=False)]))
+
+    def check(got, qa, qb, label):
+        rows, cols = pick(qa.outer), pick(qb.outer)
+        c, b = oracle.gemm(qa, qb, rows, cols)
+        sub = got[torch.as_tensor(rows, device=got.device)][:, torch.as_tensor(cols, device=got.device)]
+        _within_bf16(sub, c, b, label)
+
+    check(y.detach(), oracle.quantize(xc, axis=1), oracle.quantize(wc, axis=1), "y")
+    check(x.grad, oracle.quantize(dyc, axis=1, rounding=oracle.SR, seed=0x5EED, offset=0),
+          oracle.quantize(wc, axis=0), "dx")
+    check(layer.weight.grad, oracle.quantize(dyc, axis=0, rounding=oracle.SR, seed=0x5EED, offset=1, rht=True,
+                                             sign_mask=MASK),
+          oracle.quantize(xc, axis=0, rht=True, sign_mask=MASK), "dW")
