@@ -23,6 +23,7 @@
 //    each thread two adjacent columns and four consecutive blocks: rows are
 //    read as 1 KB contiguous runs per workgroup and each output row gets 32
 //    code bytes and 4 scale bytes from one thread.
+#include "gemm_common.h"
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -403,6 +404,133 @@ __global__ void __launch_bounds__(kQT) k_dequant(const uint2 *codes, const uint8
   }
 }
 
+// ------------------------------------------------------ dual encode ----
+//
+// Both layouts of x from one read: a workgroup stages a 64-row x 256-column
+// tile in LDS, then encodes it along the rows (axis-1 output: every thread
+// four consecutive blocks of one row, so four adjacent threads write the
+// tile's whole 128-byte code line of that row) and down the columns (axis-0
+// output, optionally after the transform: every thread the four 16-row
+// blocks of one column, 32 contiguous code bytes).  Bit-identical to the two
+// single-layout encodes: the same block scales, multipliers and counter
+// indices (block b of output o: elements 16b .. 16b+15 of the output
+// layout).  Tiles are dealt to the XCDs in contiguous ranges, ordered so that
+// the four row tiles sharing one 128-byte axis-0 output line (256 rows) are
+// consecutive and so run together on one XCD: its L2 then merges their four
+// 32-byte pieces into whole lines before writing them back.  Row tiles run
+// from the end of x back (the amax pass went forwards).
+constexpr int kDualRows = 64, kDualCols = 256;
+
+template <typename T, bool SR1, bool SR0, bool RHT0>
+__global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, int64_t cols, uint64_t seed1,
+                                                   uint64_t offset1, float *meta1, uint2 *codes1, uint8_t *scales1,
+                                                   uint32_t sign_mask0, uint64_t seed0, uint64_t offset0,
+                                                   float *meta0, uint2 *codes0, uint8_t *scales0) {
+  constexpr int E = 16 / (int)sizeof(T);                    // elements per 16-byte chunk
+  constexpr int kPitch = kDualCols * (int)sizeof(T) + 16;   // LDS row pitch (bytes), padded
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kDualRows * kPitch];
+  const int t = threadIdx.x;
+  const int tiles_r = (int)((rows + kDualRows - 1) / kDualRows), tiles_c = (int)((cols + kDualCols - 1) / kDualCols);
+  int tr, tc;
+  xcd_tile(blockIdx.x, tiles_r, tiles_c, 4, tr, tc);
+  const int64_t r0 = (int64_t)(tiles_r - 1 - tr) * kDualRows, c0 = (int64_t)tc * kDualCols;
+  const TensorScales ts1 = tensor_scales(meta1[0]), ts0 = tensor_scales(meta0[0]);
+  if (blockIdx.x == 0 && t == 0) {
+    meta1[1] = ts1.g;
+    meta0[1] = ts0.g;
+  }
+  // ---- stage the tile (rows past `rows` and chunks past `cols` skipped:
+  // no block that reads them is encoded)
+  constexpr int kChunksRow = kDualCols / E;
+#pragma unroll
+  for (int i = 0; i < kDualRows * kChunksRow / kQT; ++i) {
+    const int q = i * kQT + t, row = q / kChunksRow, ch = q % kChunksRow;
+    const int64_t gr = r0 + row, gc = c0 + (int64_t)ch * E;
+    if (gr < rows && gc < cols)
+      *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 16) =
+          *reinterpret_cast<const uint4 *>(x + gr * cols + gc);
+  }
+  __syncthreads();
+  const int64_t nb1 = cols / 16, nb0 = rows / 16;
+  // ---- axis 1: row t/4, blocks 4*(t%4) .. +3 of the tile
+  {
+    const int row = t >> 2, cb0 = 4 * (t & 3);
+    const int64_t gr = r0 + row;
+    uint2 cw[4];
+    uint32_t sc = 0;
+    int nvalid = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t gc = c0 + 16 * (cb0 + i);
+      if (gr >= rows || gc >= cols) break;
+      float y[16];
+      const T *src = reinterpret_cast<const T *>(tile + row * kPitch) + 16 * (cb0 + i);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(src[j]);
+      float m;
+      const uint32_t S = block_scale(absmax_bits16(y), ts1, &m);
+      cw[i] = encode16<SR1>(y, m, (uint64_t)(gr * nb1 + gc / 16), seed1, offset1);
+      sc |= S << (8 * i);
+      nvalid = i + 1;
+    }
+    const int64_t b = gr * nb1 + (c0 / 16 + cb0);
+    if (nvalid == 4 && (b & 1) == 0) {
+      uint4 *dst = reinterpret_cast<uint4 *>(codes1 + b);
+      dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
+      dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nvalid) codes1[b + i] = cw[i];
+    }
+    if (nvalid == 4 && (b & 3) == 0) {
+      *reinterpret_cast<uint32_t *>(scales1 + b) = sc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nvalid) scales1[b + i] = (uint8_t)(sc >> (8 * i));
+    }
+  }
+  // ---- axis 0: column t, the tile's four 16-row blocks
+  {
+    const int64_t gc = c0 + t;
+    uint2 cw[4];
+    uint32_t sc = 0;
+    int nvalid = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t gr = r0 + 16 * i;
+      if (gc >= cols || gr >= rows) break;
+      float y[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(*reinterpret_cast<const T *>(tile + (16 * i + j) * kPitch + t * (int)sizeof(T)));
+      if (RHT0) rht16(y, sign_mask0);
+      float m;
+      const uint32_t S = block_scale(absmax_bits16(y), ts0, &m);
+      cw[i] = encode16<SR0>(y, m, (uint64_t)(gc * nb0 + gr / 16), seed0, offset0);
+      sc |= S << (8 * i);
+      nvalid = i + 1;
+    }
+    const int64_t b = gc * nb0 + r0 / 16;
+    if (nvalid == 4 && (b & 1) == 0) {
+      uint4 *dst = reinterpret_cast<uint4 *>(codes0 + b);
+      dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
+      dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nvalid) codes0[b + i] = cw[i];
+    }
+    if (nvalid == 4 && (b & 3) == 0) {
+      *reinterpret_cast<uint32_t *>(scales0 + b) = sc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nvalid) scales0[b + i] = (uint8_t)(sc >> (8 * i));
+    }
+  }
+}
+
 // ------------------------------------------------------------ launches ----
 
 inline unsigned grid_for(int64_t work, int64_t per_block = kQT, int64_t cap = 1 << 20) {
@@ -538,9 +666,29 @@ hipError_t launch_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_
     if (bf16) hipLaunchKernelGGL(k_amax_dual_cols<uint16_t>, tiles, dim3(kQT), 0, stream, (const uint16_t *)x, rows, cols, sign_mask0, bits1, bits0);
     else hipLaunchKernelGGL(k_amax_dual_cols<float>, tiles, dim3(kQT), 0, stream, (const float *)x, rows, cols, sign_mask0, bits1, bits0);
   }
-  // pass 2: the two encodes
-  launch_encode(x, bf16, rows, cols, 1, rounding1, seed1, offset1, false, 0u, codes1, scales1, meta1, stream);
-  launch_encode(x, bf16, rows, cols, 0, rounding0, seed0, offset0, rht0, sign_mask0, codes0, scales0, meta0, stream);
+  // pass 2: both encodes from one read
+  const int64_t ntiles = ((cols + kDualCols - 1) / kDualCols) * ((rows + kDualRows - 1) / kDualRows);
+  if (ntiles > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 dtiles((unsigned)ntiles);
+  const bool sr1 = rounding1 == 1, sr0 = rounding0 == 1;
+#define NVFP4_QDUAL(T, S1, S0, R0)                                                                          \
+  hipLaunchKernelGGL((k_quant_dual<T, S1, S0, R0>), dtiles, dim3(kQT), 0, stream, (const T *)x, rows, cols, seed1, \
+                     offset1, meta1, (uint2 *)codes1, scales1, sign_mask0, seed0, offset0, meta0, (uint2 *)codes0,   \
+                     scales0)
+#define NVFP4_QDUAL_T(T)                                                                       \
+  do {                                                                                         \
+    if (sr1) {                                                                                 \
+      if (sr0) { if (rht0) NVFP4_QDUAL(T, true, true, true); else NVFP4_QDUAL(T, true, true, false); }     \
+      else { if (rht0) NVFP4_QDUAL(T, true, false, true); else NVFP4_QDUAL(T, true, false, false); }       \
+    } else {                                                                                   \
+      if (sr0) { if (rht0) NVFP4_QDUAL(T, false, true, true); else NVFP4_QDUAL(T, false, true, false); }   \
+      else { if (rht0) NVFP4_QDUAL(T, false, false, true); else NVFP4_QDUAL(T, false, false, false); }     \
+    }                                                                                          \
+  } while (0)
+  if (bf16) NVFP4_QDUAL_T(uint16_t);
+  else NVFP4_QDUAL_T(float);
+#undef NVFP4_QDUAL_T
+#undef NVFP4_QDUAL
   return hipGetLastError();
 }
 

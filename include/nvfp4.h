@@ -161,13 +161,14 @@ int nvfp4_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, 
  * gradients).  Equivalent, bit for bit, to
  *   nvfp4_quantize(x, x_dtype, rows, cols, 1, rounding1, seed1, offset1, out1)
  * followed by nvfp4_quantize (rht0 == 0) or nvfp4_rht_quantize (rht0 == 1)
- * of x with axis 0, rounding0, seed0, offset0, sign_mask0 into out0; the
- * amax pass reads x once for both maxima (the plain one, and the one after
- * the column transform).
+ * of x with axis 0, rounding0, seed0, offset0, sign_mask0 into out0, but
+ * each of the two passes reads x once for both layouts: the amax pass takes
+ * both maxima (the plain one, and the one after the column transform), the
+ * encode pass writes both outputs from one tile of x staged in LDS.
  *  rows % 16 == 0 and cols % 16 == 0 (both layouts need whole blocks);
  *  out1: outer = rows, k = cols; out0: outer = cols, k = rows; out1->meta and
  *  out0->meta must be different words (NVFP4_ERR_SHAPE otherwise) and the
- *  outputs must not overlap each other or x.  Enqueues four kernels.
+ *  outputs must not overlap each other or x.  Enqueues three kernels.
  */
 int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols,
                         int rounding1, uint64_t seed1, uint64_t offset1, nvfp4_tensor *out1,
