@@ -190,6 +190,18 @@ def main():
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
     torch.cuda.synchronize()
+    # measured ceilings beside the published peaks: the same device copy
+    # (read + write), and the MFMA form of the GEMM on its operand values
+    copy_ms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        calib_dst.copy_(calib_src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    measured_peaks = {"hbm_copy_GB/s": round(2 * CALIB_BYTES / (sorted(copy_ms)[2] * 1e-3) / 1e9, 1),
+                      "mfma_f16_probe_TFLOP/s": round(max(nv.nvfp4_probe_mfma(2000) for _ in range(3)), 1)}
     del calib_src, calib_dst
 
     # outputs preallocated: the timed loop allocates nothing
@@ -275,7 +287,8 @@ def main():
                 "kernel": DOMINANT + " (f32 out), avg of the dgrad and wgrad launches",
                 "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flop,
                 "algorithmic_bytes_per_launch": int(np.mean([gemm_bytes(D), gemm_bytes(Wg)])),
-                "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4)}
+                "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4),
+                "frac_of_measured_mfma_probe": round(achieved / measured_peaks["mfma_f16_probe_TFLOP/s"], 4)}
 
     # ------------------------------------------------ quantizer sweep ----
     sweep = None
@@ -432,6 +445,7 @@ def main():
                    "gemm_flop_per_step": step_flops, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "measured_peaks": measured_peaks,
         "breakdown": breakdown,
         "quantize_sweep_32768x8192_bf16": sweep,
         "fprop_quantize_warm_vs_flushed": fprop_cache,

@@ -44,7 +44,8 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_quantize_dual",
-           "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string")
+           "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_probe_mfma",
+           "nvfp4_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_dequantize.restype = ci
         L.nvfp4_gemm.argtypes = [pt, pt, vp, ci, i64, vp]
         L.nvfp4_gemm.restype = ci
+        L.nvfp4_probe_mfma.argtypes = [i64, vp, vp]
+        L.nvfp4_probe_mfma.restype = ci
         L.nvfp4_status_string.argtypes = [ci]
         L.nvfp4_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -316,6 +319,23 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: tor
         _check(lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
                                 _stream_handle(stream, dev)), "nvfp4_gemm")
     return out
+
+
+def nvfp4_probe_mfma(iters: int, stream=None) -> float:
+    """Run the MFMA ceiling probe (include/nvfp4.h) once on the current device
+    and return its rate in TFLOP/s, timed with events on the probe's stream.
+    A measurement helper for the benchmark, not part of the method."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty(1024 * 256, dtype=torch.float32, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        _check(lib().nvfp4_probe_mfma(min(iters, 8), out.data_ptr(), _stream_handle(s, dev)), "nvfp4_probe_mfma")
+        e0.record(s)
+        _check(lib().nvfp4_probe_mfma(iters, out.data_ptr(), _stream_handle(s, dev)), "nvfp4_probe_mfma")
+        e1.record(s)
+    e1.synchronize()
+    return 1024 * 4 * iters * 32 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 class MXFP4Tensor:

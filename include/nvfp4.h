@@ -246,6 +246,17 @@ int mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int a
 int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int c_dtype,
                int64_t ldc, void *hip_stream);
 
+/*
+ * nvfp4_probe_mfma -- measurement helper, not part of the method: launches
+ * 1024 workgroups of 256 threads that run `iters` x 32 v_mfma_f32_32x32x16_f16
+ * per wave (one wave per SIMD, sixteen accumulators) on operands with the
+ * values the NVFP4 GEMM multiplies (E2M1 codes times E4M3 block scales), with
+ * no memory traffic, giving the ceiling of that MFMA on that data.  Work:
+ * 1024 * 4 * iters * 32 * 32768 flop.  out: device, 1024 * 256 floats (the
+ * per-thread sums, which keep the work live).
+ */
+int nvfp4_probe_mfma(int64_t iters, float *out, void *hip_stream);
+
 /* Human-readable name of a status code (static string). */
 const char *nvfp4_status_string(int status);
 

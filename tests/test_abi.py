@@ -191,3 +191,10 @@ def test_size_limits_are_shape_errors(L):
     assert L.mxfp4_gemm(by(_mx(4, k)), by(_mx(4, k)), FAKE, 0, 4, None) == -2
     big = 1 << 40                                        # more tiles than a grid holds
     assert L.nvfp4_gemm(by(_t(big, 16)), by(_t(big, 16)), FAKE, 0, big, None) == -2
+
+
+@_no_gpu
+def test_probe_argument_errors(L):
+    assert L.nvfp4_probe_mfma(10, None, None) == -1
+    assert L.nvfp4_probe_mfma(-1, FAKE, None) == -2
+    assert L.nvfp4_probe_mfma(10, FAKE + 2, None) == -5

@@ -203,3 +203,11 @@ def test_binding_rejects_bad_buffers():
         nv.nvfp4_dequantize(qa, out=torch.empty((64, 63), device="cuda"))
     with pytest.raises(nv.NVFP4Error, match="meta"):
         nv.nvfp4_gemm(nv.NVFP4Tensor(qa.codes, qa.scales, qa.meta.double(), 64, 64), qb)
+
+
+def test_mfma_probe_runs():
+    """The MFMA ceiling probe the benchmark reports beside the published
+    peak: a finite rate below that peak (2.5 PFLOP/s dense f16)."""
+    nv = _nv()
+    rate = nv.nvfp4_probe_mfma(200)
+    assert 100.0 < rate < 2600.0, rate
