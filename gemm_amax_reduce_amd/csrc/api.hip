@@ -18,8 +18,13 @@ constexpr int64_t kMaxRowsAxis0Mx = 65535LL * 8 * 32;     // 16 776 960
 // offsets below 2^31, and launch at most INT32_MAX workgroups (tiles of
 // 256 x 128 or larger).
 constexpr int64_t kMaxGemmK = (1LL << 25) - 16;
+// Element counts (rows x cols, outer x k, M x ldc) stay at or below 2^60, so
+// every byte offset the kernels form fits in int64.
+constexpr int64_t kMaxCount = 1LL << 60;
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline bool count_ok(int64_t a, int64_t b) { return a <= 0 || b <= kMaxCount / a; }
 
 inline bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
   if (K > kMaxGemmK) return false;
@@ -32,7 +37,7 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_
 
 int check_tensor(const nvfp4_tensor *t) {
   if (!t || !t->meta) return NVFP4_ERR_NULL;
-  if (t->outer < 0 || t->k < 0 || t->k % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (t->outer < 0 || t->k < 0 || t->k % 16 != 0 || !count_ok(t->outer, t->k)) return NVFP4_ERR_SHAPE;
   if (t->outer > 0 && t->k > 0 && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
   if (!aligned(t->codes, 8) || !aligned(t->meta, 4)) return NVFP4_ERR_ALIGN;
   return NVFP4_OK;
@@ -45,7 +50,7 @@ int quantize_common(const void *x, int x_dtype, int64_t rows, int64_t cols, int 
   if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
   if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_ENUM;
   if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
-  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || !count_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   const int64_t outer = axis ? rows : cols;
   const int64_t k = axis ? cols : rows;
   if (k % 16 != 0) return NVFP4_ERR_SHAPE;
@@ -80,7 +85,7 @@ int nvfp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis,
   if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
   if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
   if (rht != 0 && rht != 1) return NVFP4_ERR_ENUM;
-  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || !count_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   if ((axis ? cols : rows) % 16 != 0) return NVFP4_ERR_SHAPE;
   if (axis == 0 && rows > kMaxRowsAxis0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
@@ -97,7 +102,7 @@ int nvfp4_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_ENUM;
   if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
   if (rht != 0 && rht != 1) return NVFP4_ERR_ENUM;
-  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || !count_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   const int64_t outer = axis ? rows : cols;
   const int64_t k = axis ? cols : rows;
   if (k % 16 != 0) return NVFP4_ERR_SHAPE;
@@ -120,7 +125,7 @@ int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   if ((rounding1 != NVFP4_RNE && rounding1 != NVFP4_SR) || (rounding0 != NVFP4_RNE && rounding0 != NVFP4_SR))
     return NVFP4_ERR_ENUM;
   if (rht0 != 0 && rht0 != 1) return NVFP4_ERR_ENUM;
-  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0 || !count_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   if (out1->outer != rows || out1->k != cols || out0->outer != cols || out0->k != rows) return NVFP4_ERR_SHAPE;
   if (rows > kMaxRowsAxis0) return NVFP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_ERR_NULL;
@@ -141,7 +146,7 @@ int mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int a
   if (!out) return NVFP4_ERR_NULL;
   if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
   if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
-  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || !count_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   const int64_t outer = axis ? rows : cols, k = axis ? cols : rows;
   if (k % 32 != 0 || out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
   if (axis == 0 && rows > kMaxRowsAxis0Mx) return NVFP4_ERR_SHAPE;
@@ -154,12 +159,16 @@ int mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int a
 int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int c_dtype, int64_t ldc, void *hip_stream) {
   if (!a || !b) return NVFP4_ERR_NULL;
   if (a->outer < 0 || b->outer < 0 || a->k < 0 || a->k != b->k || a->k % 256 != 0) return NVFP4_ERR_SHAPE;
+  if (!count_ok(a->outer, a->k) || !count_ok(b->outer, b->k)) return NVFP4_ERR_SHAPE;
   if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
   const int64_t M = a->outer, N = b->outer;
-  if (ldc < N || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
+  if (ldc < N || !count_ok(M, ldc) || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
   if (M > 0 && N > 0 && (!c || (a->k > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
     return NVFP4_ERR_NULL;
   if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
+  // the kernel moves codes in 16-byte and scales in 4-byte pieces by DMA
+  if (!aligned(a->codes, 16) || !aligned(b->codes, 16) || !aligned(a->scales, 4) || !aligned(b->scales, 4))
+    return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_mx_gemm(a->codes, a->scales, b->codes, b->scales, M, N, a->k, c, c_dtype, ldc,
                                           (hipStream_t)hip_stream));
 }
@@ -182,9 +191,11 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
   if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
   if (a->k != b->k) return NVFP4_ERR_SHAPE;
   const int64_t M = a->outer, N = b->outer;
-  if (ldc < N || ldc < 0 || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
+  if (ldc < N || !count_ok(M, ldc) || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
   if (M > 0 && N > 0 && !c) return NVFP4_ERR_NULL;
   if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
+  // with K % 64 == 0 the kernel moves the scale rows by DMA in whole dwords
+  if (a->k % 64 == 0 && (!aligned(a->scales, 4) || !aligned(b->scales, 4))) return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_gemm(a->codes, a->scales, a->meta, b->codes, b->scales, b->meta, M, N, a->k, c,
                                        c_dtype, ldc, (hipStream_t)hip_stream));
 }

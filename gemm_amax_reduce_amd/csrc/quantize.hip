@@ -35,6 +35,10 @@ namespace {
 
 constexpr int kQT = kQuantThreads;
 
+// Wide stores are taken only where the destination address itself is
+// aligned: output buffers need only the alignment of their element type.
+__device__ __forceinline__ bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
@@ -342,7 +346,7 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
   for (int e = 0; e < CPT; ++e) {
     if (c + e >= cols) break;
     const int64_t blk0 = (c + e) * nkb + kb0;
-    if (nb == kNBT && (blk0 % 2) == 0) {
+    if (nb == kNBT && aligned_to(codes + blk0, 16)) {
       uint4 *dst = reinterpret_cast<uint4 *>(codes + blk0);
       dst[0] = make_uint4(cw[e][0].x, cw[e][0].y, cw[e][1].x, cw[e][1].y);
       dst[1] = make_uint4(cw[e][2].x, cw[e][2].y, cw[e][3].x, cw[e][3].y);
@@ -351,7 +355,7 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
       for (int i = 0; i < kNBT; ++i)
         if (i < nb) codes[blk0 + i] = cw[e][i];
     }
-    if (nb == kNBT && (blk0 % 4) == 0) {
+    if (nb == kNBT && aligned_to(scales + blk0, 4)) {
       *reinterpret_cast<uint32_t *>(scales + blk0) = sc[e];
     } else {
 #pragma unroll
@@ -474,7 +478,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
       nvalid = i + 1;
     }
     const int64_t b = gr * nb1 + (c0 / 16 + cb0);
-    if (nvalid == 4 && (b & 1) == 0) {
+    if (nvalid == 4 && aligned_to(codes1 + b, 16)) {
       uint4 *dst = reinterpret_cast<uint4 *>(codes1 + b);
       dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
       dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
@@ -483,7 +487,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
       for (int i = 0; i < 4; ++i)
         if (i < nvalid) codes1[b + i] = cw[i];
     }
-    if (nvalid == 4 && (b & 3) == 0) {
+    if (nvalid == 4 && aligned_to(scales1 + b, 4)) {
       *reinterpret_cast<uint32_t *>(scales1 + b) = sc;
     } else {
 #pragma unroll
@@ -512,7 +516,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
       nvalid = i + 1;
     }
     const int64_t b = gc * nb0 + r0 / 16;
-    if (nvalid == 4 && (b & 1) == 0) {
+    if (nvalid == 4 && aligned_to(codes0 + b, 16)) {
       uint4 *dst = reinterpret_cast<uint4 *>(codes0 + b);
       dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
       dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
@@ -521,7 +525,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
       for (int i = 0; i < 4; ++i)
         if (i < nvalid) codes0[b + i] = cw[i];
     }
-    if (nvalid == 4 && (b & 3) == 0) {
+    if (nvalid == 4 && aligned_to(scales0 + b, 4)) {
       *reinterpret_cast<uint32_t *>(scales0 + b) = sc;
     } else {
 #pragma unroll

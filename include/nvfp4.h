@@ -30,7 +30,8 @@
  *    Limits of the launch geometry (NVFP4_ERR_SHAPE beyond them):
  *    quantization down the columns (axis 0, and the dual call) takes
  *    rows <= 4 194 240 (MXFP4: 16 776 960); the GEMMs take K <= 2^25 - 16
- *    and ceil(M/256) * ceil(N/128) <= INT32_MAX.
+ *    and ceil(M/256) * ceil(N/128) <= INT32_MAX; every element count
+ *    (rows * cols, outer * k, M * ldc) is at most 2^60.
  *  - Element types: NVFP4_F32 (binary32) or NVFP4_BF16 (bfloat16).
  *  - Thread safety: stateless; concurrent calls on different outputs are
  *    fine.  The calls keep no scratch memory between launches.
@@ -65,7 +66,9 @@ typedef enum { NVFP4_RNE = 0, NVFP4_SR = 1 } nvfp4_rounding;
  *           bit 3 sign, bits 0-2 the magnitude 0, .5, 1, 1.5, 2, 3, 4, 6.
  *           8-byte aligned.
  *  scales : u8 [outer][k/16]; the OCP E4M3FN block scale of each 16-element
- *           block along k (never NaN, at most 448).
+ *           block along k (never NaN, at most 448).  4-byte aligned when k %
+ *           64 == 0 and the tensor is a GEMM operand (whole scale dwords move
+ *           by DMA then); any alignment otherwise.
  *  meta   : f32 [2]; meta[0] = amax (the tensor maximum magnitude after the
  *           optional transform), meta[1] = g = amax / 2688, the FP32 decode
  *           scale.  4-byte aligned.
@@ -214,7 +217,7 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
  *  codes  : u8 [outer][k/2], E2M1 codes two per byte (element 2j low
  *           nibble), 16-byte aligned.
  *  scales : u8 [outer][k/32], E8M0 exponents: the block scale is
- *           2^(code - 127).
+ *           2^(code - 127).  4-byte aligned for a GEMM operand.
  *  outer, k : k % 32 == 0.
  * The value of element (o, kk) is e2m1(code) * 2^(scale - 127).
  */

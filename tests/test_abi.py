@@ -96,6 +96,12 @@ def test_gemm_argument_errors(L):
     assert L.nvfp4_gemm(by(a), by(b), None, 0, 4, None) == -1             # C NULL
     assert L.nvfp4_gemm(by(a), by(b), FAKE + 2, 0, 4, None) == -5         # C misaligned (f32)
     assert L.nvfp4_gemm(by(_t(-1, 32)), by(b), FAKE, 0, 4, None) == -2
+    # K % 64 == 0: scale rows move by DMA in whole dwords, so scales must be
+    # 4-byte aligned; other K read them byte by byte (any alignment)
+    a64, b64 = _t(8, 64, scales=FAKE + 1), _t(4, 64)
+    assert L.nvfp4_gemm(by(a64), by(b64), FAKE, 0, 4, None) == -5
+    assert L.nvfp4_gemm(by(_t(8, 64)), by(_t(4, 64, scales=FAKE + 2)), FAKE, 0, 4, None) == -5
+    assert L.nvfp4_gemm(by(_t(8, 48, scales=FAKE + 1)), by(_t(4, 48)), None, 0, 4, None) == -1  # not an ALIGN error
 
 
 def test_binding_refuses_cpu_tensors():
@@ -168,6 +174,8 @@ def test_mxfp4_argument_errors(L):
     assert L.mxfp4_gemm(by(a), by(b), FAKE, 2, 4, None) == -3              # dtype
     assert L.mxfp4_gemm(by(a), by(b), FAKE, 0, 3, None) == -2              # ldc < N
     assert L.mxfp4_gemm(by(a), by(b), None, 0, 4, None) == -1              # c NULL
+    assert L.mxfp4_gemm(by(_mx(8, 256, codes=FAKE + 8)), by(b), FAKE, 0, 4, None) == -5   # codes: 16 B
+    assert L.mxfp4_gemm(by(a), by(_mx(4, 256, scales=FAKE + 2)), FAKE, 0, 4, None) == -5  # scales: 4 B
 
 
 @_no_gpu
@@ -191,6 +199,17 @@ def test_size_limits_are_shape_errors(L):
     assert L.mxfp4_gemm(by(_mx(4, k)), by(_mx(4, k)), FAKE, 0, 4, None) == -2
     big = 1 << 40                                        # more tiles than a grid holds
     assert L.nvfp4_gemm(by(_t(big, 16)), by(_t(big, 16)), FAKE, 0, big, None) == -2
+    # element counts above 2^60 (rows * cols, outer * k, M * ldc)
+    r = c = 1 << 31
+    assert L.nvfp4_quantize(FAKE, 1, r, c, 1, 0, 0, 0, by(_t(r, c)), None) == -2
+    assert L.nvfp4_amax(FAKE, 1, r, c, 1, 0, 0, FAKE, None) == -2
+    assert L.nvfp4_quantize_amax(FAKE, 1, r, c, 1, 0, 0, 0, 0, 0, FAKE, by(_t(r, c)), None) == -2
+    assert L.nvfp4_quantize_dual(FAKE, 1, r, c, 0, 0, 0, by(_t(r, c)), 0, 0, 0, 0, 0,
+                                 by(_t(c, r, meta=FAKE + 64)), None) == -2
+    assert L.mxfp4_quantize(FAKE, 1, r, c, 1, by(_mx(r, c)), None) == -2
+    assert L.nvfp4_dequantize(by(_t(r, c)), FAKE, 0, None) == -2
+    assert L.nvfp4_gemm(by(_t(1 << 20, 16)), by(_t(4, 16)), FAKE, 0, 1 << 41, None) == -2
+    assert L.mxfp4_gemm(by(_mx(1 << 20, 256)), by(_mx(4, 256)), FAKE, 0, 1 << 41, None) == -2
 
 
 @_no_gpu
