@@ -82,10 +82,16 @@ class NVFP4Linear(torch.nn.Module):
         self._calls = 0
 
     def forward(self, x):
+        """x [..., in] -> [..., out]; the leading dimensions are the tokens."""
         if self.keep_bf16:
             return torch.nn.functional.linear(x.to(torch.bfloat16), self.weight.to(torch.bfloat16)).to(x.dtype)
-        if x.shape[0] % 16:
+        if x.dim() < 1 or x.shape[-1] != self.weight.shape[1]:
+            raise NVFP4Error(f"x must end in {self.weight.shape[1]} features, got shape {tuple(x.shape)}")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1])
+        if x2.shape[0] % 16:
             raise NVFP4Error("the token count must be a multiple of 16 (the weight gradient reduces over it)")
         offset = self._calls
         self._calls += 1
-        return NVFP4LinearFunction.apply(x, self.weight, self.seed, offset, self.sign_mask)
+        y = NVFP4LinearFunction.apply(x2, self.weight, self.seed, offset, self.sign_mask)
+        return y.reshape(*lead, self.weight.shape[0])

@@ -88,6 +88,33 @@ def test_successive_calls_draw_fresh_offsets():
     assert not torch.equal(grads[0], grads[1])     # stochastic rounding differs between steps
 
 
+def test_leading_dimensions_are_tokens():
+    """x [batch, seq, in] runs as the [batch*seq, in] matrix: outputs and
+    both gradients bit-identical to the flattened call (same weight, seed and
+    step), y shaped [batch, seq, out]; a token count that is not a multiple
+    of 16 is refused."""
+    import gemm_amax_reduce_amd.linear as L
+    la = L.NVFP4Linear(96, 80, seed=4, sign_mask=MASK, device="cuda", dtype=torch.float32)
+    lb = L.NVFP4Linear(96, 80, seed=4, sign_mask=MASK, device="cuda", dtype=torch.float32)
+    with torch.no_grad():
+        lb.weight.copy_(la.weight)
+    x = torch.from_numpy(workloads.normal(48, 96, 12)).cuda()
+    x3 = x.reshape(2, 24, 96).clone().requires_grad_(True)
+    x2 = x.clone().requires_grad_(True)
+    dy = torch.from_numpy(workloads.laplace(48, 80, 13, 1e-3)).cuda()
+    y3, y2 = la(x3), lb(x2)
+    assert y3.shape == (2, 24, 80)
+    y3.backward(dy.reshape(2, 24, 80))
+    y2.backward(dy)
+    torch.cuda.synchronize()
+    assert torch.equal(y3.detach().reshape(48, 80), y2.detach())
+    assert torch.equal(x3.grad.reshape(48, 96), x2.grad)
+    assert torch.equal(la.weight.grad, lb.weight.grad)
+    import gemm_amax_reduce_amd as nv
+    with pytest.raises(nv.NVFP4Error, match="multiple of 16"):
+        la(torch.zeros(3, 5, 96, device="cuda"))
+
+
 def test_full_layer_shape_bf16():
     """The layer at the benchmark's large shape (8192 tokens, 5120 -> 20480,
     bf16): y, dx and dW on sampled rows and columns against the oracle's
