@@ -36,6 +36,11 @@ METRIC = "NVFP4 quantize GB/s + block-scaled GEMM TFLOPS (fprop/dgrad/wgrad) at 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA, published
 PEAK_FP4_TFLOPS = 10100.0       # MI355X dense fp4 MFMA, published (context)
+# The pages' chip-level matmul figures for NVIDIA GB300 (the Thinking Machines
+# article, section on the three formats of one training run): context only,
+# another machine's numbers, dense or sparse not stated.
+PAGES_CONTEXT = {"platform": "NVIDIA GB300", "nvfp4_PFLOP/s": 15.0, "mxfp8_PFLOP/s": 5.0, "bf16_PFLOP/s": 2.5,
+                 "nvfp4_over_bf16": 6.0, "note": "chip-level figures quoted by the pages; not targets"}
 
 
 def qbytes(n_elem: int, in_bytes: int) -> int:
@@ -451,10 +456,23 @@ def main():
         "fprop_quantize_warm_vs_flushed": fprop_cache,
         "bf16_gemm_context": bf16_ctx,
         "mxfp4_step_context": mx_ctx,
+        "pages_context": PAGES_CONTEXT,
         "device": torch.cuda.get_device_name(0),
         "step_ms_event_median": round(float(np.median(step_ms)), 4),
     }
     print(json.dumps(rec), flush=True)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(F, D, Wg, mask, seed, step_flops):
@@ -487,7 +505,7 @@ def cpu_baseline(F, D, Wg, mask, seed, step_flops):
         t_g += (time.perf_counter() - t) * m / rows_sample
     t_step = t_q + t_g
     return {"value": round(step_flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"all six operand quantizations in full ({t_q:.1f}s) + oracle GEMM on {rows_sample} output "
                       f"rows of each GEMM, extrapolated to the full M ({t_g:.1f}s est.); step {t_step:.1f}s",
             "ms_per_step_est": round(t_step * 1e3, 1)}
