@@ -143,6 +143,86 @@ def reduce_traffic(fetch_dir: str, write_dir: str) -> dict:
             "bytes_per_launch": fetch_b + write_b, "dispatches": [len(fetch["dominant"]), len(write["dominant"])]}
 
 
+QUANT_PROFILE = os.path.join(ROOT, "profiles", "quantizer_sweep_32768x8192_counters.md")
+SWEEP_VARIANTS = [(axis, rnd, rht) for axis in (1, 0) for rnd in ("rne", "sr") for rht in (False, True)]
+SWEEP_CALLS = 12          # 2 warm-up + 10 timed calls per variant
+
+
+def _dispatches(d):
+    """Per-dispatch rows of a rocprofv3 --pmc run: [(name, grid, start, end, {counter: value})] in order."""
+    import csv
+    import glob
+    disp = {}
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(fn)):
+            k = int(r["Dispatch_Id"])
+            e = disp.setdefault(k, [r["Kernel_Name"], int(r["Grid_Size"]), int(r["Start_Timestamp"]),
+                                    int(r["End_Timestamp"]), {}])
+            e[4][r["Counter_Name"]] = float(r["Counter_Value"])
+    return [disp[k] for k in sorted(disp)]
+
+
+def reduce_quant_counters(fetch_dir: str, write_dir: str, valu_dir: str) -> str:
+    """Per-pass HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by the calibration
+    copy), time and VALU busy of the quantizer sweep's calls, from three
+    rocprofv3 --pmc runs of this script; returns the markdown summary."""
+    n = 32768 * 8192
+    runs = {}
+    for tag, d in (("fetch", fetch_dir), ("write", write_dir), ("valu", valu_dir)):
+        ds = _dispatches(d)
+        first = next(i for i, e in enumerate(ds)
+                     if "k_quant_rows<unsigned short, false, false>" in e[0] and e[1] == n // 16)
+        seq = ds[first - 2: first - 2 + 3 * SWEEP_CALLS * len(SWEEP_VARIANTS)]
+        for v, (axis, rnd, rht) in enumerate(SWEEP_VARIANTS):
+            amax = "k_amax_rht_" + ("rows" if axis else "cols") if rht else "k_amax_flat"
+            enc = "k_quant_%s<unsigned short, %s, %s>" % ("rows" if axis else "cols", str(rnd == "sr").lower(),
+                                                          str(rht).lower())
+            for c in range(SWEEP_CALLS):
+                trio = seq[3 * (v * SWEEP_CALLS + c): 3 * (v * SWEEP_CALLS + c) + 3]
+                if not ("k_meta_init" in trio[0][0] and amax in trio[1][0] and enc in trio[2][0]):
+                    raise SystemExit(f"--quant-counters: unexpected dispatch order in {d} at variant {v} call {c}")
+        runs[tag] = (ds, seq)
+    copies = [e for e in runs["fetch"][0] if "copyBuffer" in e[0]]
+    f_scale = CALIB_BYTES / (max(e[4]["FETCH_SIZE"] for e in copies) * 1024.0)
+    copies = [e for e in runs["write"][0] if "copyBuffer" in e[0]]
+    w_scale = CALIB_BYTES / (max(e[4]["WRITE_SIZE"] for e in copies) * 1024.0)
+    alg_read, alg_write = 2 * n, n // 2 + n // 16
+    rows = []
+    for v, (axis, rnd, rht) in enumerate(SWEEP_VARIANTS):
+        for p, pname in ((1, "amax"), (2, "encode")):
+            idx = [3 * (v * SWEEP_CALLS + c) + p for c in range(SWEEP_CALLS)]
+            fe = [runs["fetch"][1][i] for i in idx]
+            we = [runs["write"][1][i] for i in idx]
+            va = [runs["valu"][1][i] for i in idx]
+            us = sum((e[3] - e[2]) / 1e3 for e in fe) / len(fe)
+            rd = sum(e[4]["FETCH_SIZE"] for e in fe) / len(fe) * 1024.0 * f_scale
+            wr = sum(e[4]["WRITE_SIZE"] for e in we) / len(we) * 1024.0 * w_scale
+            busy = sum(e[4]["SQ_INSTS_VALU"] * 4 / (e[4]["GRBM_GUI_ACTIVE"] / 8 * 1024) for e in va) / len(va)
+            rows.append((f"axis{axis} {rnd}{'+rht' if rht else ''}", pname, fe[0][0].split("::")[-1].split("(")[0],
+                         us, rd, alg_read, wr, alg_write if p == 2 else 0, (rd + wr) / (us * 1e-6) / 1e9, busy))
+    run = "--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline"
+    lines = ["# Quantizer counters on the 32768x8192 bf16 sweep tensor", "",
+             "Commands (repository root, one MI355X), one counter set per run, then the reduction:", "", "```",
+             f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -d {fetch_dir} -o run {run}",
+             f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -d {write_dir} -o run {run}",
+             f"rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR "
+             f"--kernel-trace -d {valu_dir} -o run {run}",
+             f"python3 bench.py --quant-counters {fetch_dir} {write_dir} {valu_dir}", "```", "",
+             f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for the 256 MiB "
+             f"calibration copy of the same run ({f_scale:.2f} and {w_scale:.2f}). The tensor (512 MiB) exceeds the "
+             "256 MB MALL. Algorithmic bytes per call: the amax pass reads 537 MB; the encode pass reads 537 MB and "
+             "writes 151 MB of codes and scales. VALU busy = SQ_INSTS_VALU x 4 cycles / (GRBM_GUI_ACTIVE/8 x 1024 "
+             "SIMDs), the share of SIMD issue cycles spent on VALU instructions at one pass each (quarter-rate "
+             "instructions such as the 64-bit multiplies of Philox take four, so SR is undercounted). Times from "
+             f"the FETCH_SIZE run's dispatch timestamps. Averages over the {SWEEP_CALLS} calls of each variant.", "",
+             "| variant | pass | kernel | us | HBM read MB (alg.) | HBM write MB (alg.) | achieved GB/s | VALU busy |",
+             "|---|---|---|---:|---:|---:|---:|---:|"]
+    for (var, pname, kern, us, rd, ard, wr, awr, gbs, busy) in rows:
+        lines.append(f"| {var} | {pname} | {kern} | {us:.1f} | {rd / 1e6:.0f} ({ard / 1e6:.0f}) | "
+                     f"{wr / 1e6:.0f} ({awr / 1e6:.0f}) | {gbs:.0f} | {busy:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,7 +233,16 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="reduce two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script into "
                          "the traffic profile and exit (no GPU needed)")
+    ap.add_argument("--quant-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "VALU_DIR"),
+                    help="reduce three rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE, VALU counters) "
+                         "into the quantizer counter profile and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.quant_counters:
+        md = reduce_quant_counters(*args.quant_counters)
+        with open(QUANT_PROFILE, "w") as f:
+            f.write(md)
+        print(md)
+        return
     if args.traffic:
         prof = reduce_traffic(*args.traffic)
         run = "--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-sweep"
