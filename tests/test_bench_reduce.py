@@ -1,0 +1,93 @@
+"""Host logic of the benchmark's counter reductions (no GPU): the traffic
+profile of the dominant GEMM and the quantizer sweep's counter table, fed
+with synthetic rocprofv3 counter_collection.csv files."""
+import csv
+import os
+
+import pytest
+
+import bench
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+          "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+          "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+N_SWEEP = 32768 * 8192
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def write_run(d, dispatches):
+    """dispatches: [(name, grid, duration_ns, {counter: value})]"""
+    os.makedirs(d, exist_ok=True)
+    t = 1000
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, grid, dur, counters) in enumerate(dispatches, start=1):
+            for cn, cv in counters.items():
+                w.writerow({**{k: 0 for k in FIELDS}, "Dispatch_Id": i, "Grid_Size": grid, "Kernel_Name": name,
+                            "Counter_Name": cn, "Counter_Value": cv, "Start_Timestamp": t,
+                            "End_Timestamp": t + dur})
+            t += dur + 10
+
+
+def sweep_dispatches(counters_of):
+    out = []
+    for axis, rnd, rht in bench.SWEEP_VARIANTS:
+        amax = ("k_amax_rht_" + ("rows" if axis else "cols")) if rht else "k_amax_flat"
+        enc = "k_quant_%s<unsigned short, %s, %s>" % ("rows" if axis else "cols", str(rnd == "sr").lower(),
+                                                      str(rht).lower())
+        for _ in range(bench.SWEEP_CALLS):
+            out.append(("nvfp4::k_meta_init(float*)", 64, 2000, counters_of("meta")))
+            out.append((f"void nvfp4::{amax}<unsigned short>(...)", 262144, 90000, counters_of("amax")))
+            out.append((f"void nvfp4::{enc}(...)", N_SWEEP // 16, 110000, counters_of("enc")))
+    return out
+
+
+def test_quant_counter_table(tmp_path):
+    # the copy reads 2x and writes 1x its size in KiB, so the scales are 0.5 and 1
+    kib = bench.CALIB_BYTES / 1024
+    step = [("void nvfp4::k_quant_rows<unsigned short, false, false>(...)", 4096 * 5120 // 16, 30000, {})]
+    fetch = {"meta": 0.0, "amax": 2 * 2 * N_SWEEP / 1024, "enc": 2 * 2 * N_SWEEP / 1024}
+    write = {"meta": 0.0, "amax": 0.0, "enc": (N_SWEEP // 2 + N_SWEEP // 16) / 1024}
+    for tag, cname, per, copyv in (("fetch", "FETCH_SIZE", fetch, 2 * kib), ("write", "WRITE_SIZE", write, kib)):
+        disp = [(COPY, 1, 100000, {cname: copyv})]
+        disp += [(n, g, dur, {cname: 1.0}) for n, g, dur, _ in step]
+        disp += sweep_dispatches(lambda kind: {cname: per[kind]})
+        write_run(str(tmp_path / tag), disp)
+    valu = [(COPY, 1, 100000, {"GRBM_GUI_ACTIVE": 8.0, "SQ_INSTS_VALU": 0.0})]
+    valu += sweep_dispatches(lambda kind: {"GRBM_GUI_ACTIVE": 8.0 * 1000, "SQ_INSTS_VALU": 1024 * 1000 / 4 / 2})
+    write_run(str(tmp_path / "valu"), valu)
+    md = bench.reduce_quant_counters(str(tmp_path / "fetch"), str(tmp_path / "write"), str(tmp_path / "valu"))
+    rows = [l for l in md.splitlines() if l.startswith("| axis")]
+    assert len(rows) == 2 * len(bench.SWEEP_VARIANTS)
+    first_enc = rows[1].split("|")
+    assert first_enc[2].strip() == "encode" and "k_quant_rows<unsigned short, false, false>" in first_enc[3]
+    assert first_enc[4].strip() == "110.0"                         # us from the timestamps
+    assert first_enc[5].strip() == "537 (537)"                      # 2 B/element read, scaled by 0.5
+    assert first_enc[6].strip() == "151 (151)"
+    assert first_enc[8].strip() == "0.50"                           # VALU busy
+    assert "(2.00 and 1.00)" not in md and "(0.50 and 1.00)" in md
+
+
+def test_quant_counter_order_is_checked(tmp_path):
+    kib = bench.CALIB_BYTES / 1024
+    for tag, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"), ("valu", "SQ_INSTS_VALU")):
+        disp = [(COPY, 1, 100000, {cname: kib, "GRBM_GUI_ACTIVE": 8.0})]
+        sw = sweep_dispatches(lambda kind: {cname: 1.0, "GRBM_GUI_ACTIVE": 8.0})
+        sw[40], sw[41] = sw[41], sw[40]          # a dispatch out of the expected order
+        write_run(str(tmp_path / tag), disp + sw)
+    with pytest.raises(SystemExit, match="unexpected dispatch order"):
+        bench.reduce_quant_counters(str(tmp_path / "fetch"), str(tmp_path / "write"), str(tmp_path / "valu"))
+
+
+def test_traffic_reduction(tmp_path):
+    kib = bench.CALIB_BYTES / 1024
+    dom = f"void nvfp4::{bench.DOMINANT}(...)"
+    write_run(str(tmp_path / "f"), [(COPY, 1, 100, {"FETCH_SIZE": 2 * kib}), (dom, 1, 100, {"FETCH_SIZE": 1000.0}),
+                                    (dom, 1, 100, {"FETCH_SIZE": 3000.0})])
+    write_run(str(tmp_path / "w"), [(COPY, 1, 100, {"WRITE_SIZE": kib}), (dom, 1, 100, {"WRITE_SIZE": 500.0})])
+    prof = bench.reduce_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+    assert prof["fetch_scale"] == pytest.approx(0.5) and prof["write_scale"] == pytest.approx(1.0)
+    assert prof["fetch_bytes_per_launch"] == pytest.approx(2000 * 1024 * 0.5)
+    assert prof["write_bytes_per_launch"] == pytest.approx(500 * 1024)
+    assert prof["dispatches"] == [2, 1]
