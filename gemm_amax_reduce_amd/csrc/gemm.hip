@@ -154,7 +154,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
     sview_b = make_rsrc(SB + br0 * rs, (uint32_t)min<int64_t>(BN / 2, N - br0) * rs);
   }
   u32x4 codes[2][NF];      // [stage parity][fragment]: this lane's 32 codes
-  uint32_t sraw[NF];       // their two E4M3 block scales
+  uint32_t sraw[NF];       // their two E4M3 block scales (per-lane loads)
+  u32x4 srow[NF];          // scale DMA: the fragment row's 16 scale bytes of the group, as read
+  uint32_t sgrp[NF][2];    // ... this lane's two bytes of stages 0,1 and of stages 2,3
+  // byte selector of v_perm_b32: bytes 2h, 2h+1 of two scale dwords
+  const uint32_t ssel = h ? 0x07060302u : 0x05040100u;
   uint32_t keep = 0;       // which of those two scales lie inside K
   half2_t spair[NF];       // ... as an f16 pair
   half8_t opnd[2][NF];     // [K step parity][fragment]: decoded MFMA operands
@@ -181,7 +185,9 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
       const uint32_t row = f < 4 ? a_row + 32 * f : b_row + 32 * (f - 4);
       codes[cb][f] = *reinterpret_cast<const u32x4 *>(gb + row * 128 + slot);
       if constexpr (SCALE_DMA) {
-        sraw[f] = *reinterpret_cast<const uint16_t *>(gb + kCodeBytes + row * 16 + 2 * c);
+        // all four stages' scales of the group in one conflict-free 16-byte
+        // read per row (per-stage 2-byte reads put 32 rows on 8 banks)
+        if (sp == 0) srow[f] = *reinterpret_cast<const u32x4 *>(gb + kCodeBytes + row * 16);
       } else {
         const __amdgpu_buffer_rsrc_t v = f < 4 ? sview_a : sview_b;
         const uint32_t vo = (uint32_t)r * rs + 2 * h;
@@ -193,9 +199,26 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
     const int kc = kGroupK * g + 32 * c;
     keep = (kc < k32 ? 0x00FFu : 0u) | (kc + 16 < k32 ? 0xFF00u : 0u);
   };
-  auto scale_pairs = [&]() {
+  // This lane's scale bytes of the group's four stages, a K step after the
+  // 16-byte reads were issued.
+  auto pick_scales = [&]() {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) spair[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[f] & keep, 1.0f, false);
+    for (int f = 0; f < NF; ++f) {
+      sgrp[f][0] = __builtin_amdgcn_perm(srow[f].y, srow[f].x, ssel);
+      sgrp[f][1] = __builtin_amdgcn_perm(srow[f].w, srow[f].z, ssel);
+    }
+  };
+  // f16 pairs of the scales of stage sp (of the group last read).
+  auto scale_pairs = [&](auto spc) {
+    constexpr int sp = decltype(spc)::value;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if constexpr (SCALE_DMA)
+        spair[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sgrp[f][sp >> 1] & (keep << (16 * (sp & 1))), 1.0f,
+                                                            (sp & 1) != 0);
+      else
+        spair[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[f] & keep, 1.0f, false);
+    }
   };
   // Half `part` (bytes 2part, 2part+1 = 4 codes) of word ks of fragment f:
   // K step ks lies in 16-block ks/2 of the chunk.
@@ -224,7 +247,8 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   __syncthreads();
   read_stage(0, smem, 0, 0);
   __builtin_amdgcn_s_waitcnt(0);     // nothing outstanding at loop entry
-  scale_pairs();
+  if constexpr (SCALE_DMA) pick_scales();
+  scale_pairs(std::integral_constant<int, 0>{});
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     decode_half(0, 0, f, 0, 0);
@@ -261,7 +285,8 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
           dma_part(g + 1, (g + 1) & 1, P);
         }
       }
-      if (ks == 3) scale_pairs();
+      if (SCALE_DMA && P == 3 && ks == 1) pick_scales();
+      if (ks == 3) scale_pairs(std::integral_constant<int, (P + 1) & 3>{});
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         __builtin_amdgcn_sched_barrier(0);
