@@ -223,6 +223,52 @@ def reduce_quant_counters(fetch_dir: str, write_dir: str, valu_dir: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+BUSY_PROFILE = os.path.join(ROOT, "profiles", "gemm_f32_dgrad_wgrad_mfma_busy.md")
+BUSY_COUNTERS = ("GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA "
+                 "SQ_INSTS_VALU SQ_WAIT_INST_ANY SQ_LDS_BANK_CONFLICT")
+
+
+def reduce_busy(busy_dir: str) -> str:
+    """MFMA busy fraction, clock and issue counters of the GEMM kernels from
+    one rocprofv3 --pmc run of this script; returns the markdown summary."""
+    ds = _dispatches(busy_dir)
+    kinds = (("k_gemm_nvfp4<true, true>", "fprop"), ("k_gemm_nvfp4<false, true>", "dgrad + wgrad"))
+    lines = ["# MFMA busy fraction and clock of the GEMM kernels (linear-layer step)", "",
+             "Command (repository root, one MI355X; one counter pass, 7 SQ + 1 GRBM counters), then the reduction:",
+             "", "```",
+             f"rocprofv3 --pmc {BUSY_COUNTERS} --kernel-trace -d {busy_dir} -o run --output-format csv -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-sweep",
+             f"python3 bench.py --busy {busy_dir}", "```", "",
+             "Per dispatch, with G = GRBM_GUI_ACTIVE / 8 XCDs (GPU cycles of the kernel): clock = G / kernel "
+             "duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (G x 1024 SIMDs); VALU instructions per MFMA = "
+             "SQ_INSTS_VALU / SQ_INSTS_MFMA (SQ_INSTS_VALU counts the MFMAs too); VALU active = "
+             "4 x SQ_ACTIVE_INST_VALU / (G x 1024) and issue wait = 4 x SQ_WAIT_INST_ANY / (G x 1024), per-wave "
+             "fractions of the cycles (the SQ counts these in units of 4 cycles; one wave per SIMD); LDS "
+             "bank-conflict cycles per CU = SQ_LDS_BANK_CONFLICT / (G x 256). Averages over the dispatches of "
+             "the run (warm-up included).", "",
+             "| kernel | dispatches | ms | clock GHz | MFMA busy | VALU instr / MFMA | VALU active | issue wait "
+             "| LDS conflict cycles |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for key, label in kinds:
+        sel = [e for e in ds if key in e[0]]
+        if not sel:
+            raise SystemExit(f"--busy: no {key} dispatches in {busy_dir}")
+        acc = {"ms": 0.0, "ghz": 0.0, "busy": 0.0, "ipm": 0.0, "va": 0.0, "wait": 0.0, "lds": 0.0}
+        for e in sel:
+            c, dur = e[4], (e[3] - e[2]) * 1e-9
+            g = c["GRBM_GUI_ACTIVE"] / 8
+            acc["ms"] += dur * 1e3
+            acc["ghz"] += g / dur / 1e9
+            acc["busy"] += c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 1024)
+            acc["ipm"] += c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]
+            acc["va"] += 4 * c["SQ_ACTIVE_INST_VALU"] / (g * 1024)
+            acc["wait"] += 4 * c["SQ_WAIT_INST_ANY"] / (g * 1024)
+            acc["lds"] += c["SQ_LDS_BANK_CONFLICT"] / (g * 256)
+        a = {k: v / len(sel) for k, v in acc.items()}
+        lines.append(f"| {key} ({label}) | {len(sel)} | {a['ms']:.3f} | {a['ghz']:.2f} | {a['busy']:.3f} | "
+                     f"{a['ipm']:.2f} | {a['va']:.3f} | {a['wait']:.3f} | {a['lds']:.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,7 +282,16 @@ def main():
     ap.add_argument("--quant-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "VALU_DIR"),
                     help="reduce three rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE, VALU counters) "
                          "into the quantizer counter profile and exit (no GPU needed)")
+    ap.add_argument("--busy", metavar="BUSY_DIR",
+                    help="reduce a rocprofv3 --pmc run of this script with the MFMA-busy counters into the GEMM "
+                         "busy profile and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.busy:
+        md = reduce_busy(args.busy)
+        with open(BUSY_PROFILE, "w") as f:
+            f.write(md)
+        print(md)
+        return
     if args.quant_counters:
         md = reduce_quant_counters(*args.quant_counters)
         with open(QUANT_PROFILE, "w") as f:

@@ -91,3 +91,17 @@ def test_traffic_reduction(tmp_path):
     assert prof["fetch_bytes_per_launch"] == pytest.approx(2000 * 1024 * 0.5)
     assert prof["write_bytes_per_launch"] == pytest.approx(500 * 1024)
     assert prof["dispatches"] == [2, 1]
+
+
+def test_busy_reduction(tmp_path):
+    g = 2.0e6                                    # GPU cycles of the kernel (GRBM_GUI_ACTIVE / 8)
+    counters = {"GRBM_GUI_ACTIVE": 8 * g, "SQ_VALU_MFMA_BUSY_CYCLES": g * 1024 * 0.5, "SQ_BUSY_CYCLES": 1.0,
+                "SQ_ACTIVE_INST_VALU": g * 1024 / 8, "SQ_INSTS_MFMA": 10.0, "SQ_INSTS_VALU": 60.0,
+                "SQ_WAIT_INST_ANY": g * 1024 / 16, "SQ_LDS_BANK_CONFLICT": g * 256 * 0.1}
+    write_run(str(tmp_path / "b"), [("void nvfp4::k_gemm_nvfp4<true, true>(...)", 1, 1_000_000, counters),
+                                    ("void nvfp4::k_gemm_nvfp4<false, true>(...)", 1, 1_000_000, counters),
+                                    ("void nvfp4::k_gemm_nvfp4<false, true>(...)", 1, 1_000_000, counters)])
+    md = bench.reduce_busy(str(tmp_path / "b"))
+    row = [c.strip() for c in md.splitlines()[-1].split("|")]
+    # dispatches, ms, GHz, MFMA busy, VALU/MFMA, VALU active, issue wait, LDS conflict
+    assert row[2:10] == ["2", "1.000", "2.00", "0.500", "6.00", "0.500", "0.250", "0.100"]
