@@ -217,3 +217,17 @@ def test_probe_argument_errors(L):
     assert L.nvfp4_probe_mfma(10, None, None) == -1
     assert L.nvfp4_probe_mfma(-1, FAKE, None) == -2
     assert L.nvfp4_probe_mfma(10, FAKE + 2, None) == -5
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU only: --gpus above 1 exits with a message
+    before touching a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
