@@ -1,9 +1,10 @@
 """The library keeps no state between calls, so work on two streams at once
 gives the same bits as the same calls in sequence: the linear-layer step
 with the backward operands of the forward tensors (W on axis 0, X on axis 0
-with the transform) quantized on a second stream while the forward
-quantizations and GEMM run on the first, the dgrad GEMM waiting for them
-(the schedule the benchmark's step uses), against the one-stream step."""
+with the transform) quantized on a second stream, released once the forward
+quantizations are issued, while the fprop GEMM runs on the first, the dgrad
+GEMM waiting for them (the schedule the benchmark's step uses), against the
+one-stream step."""
 import pytest
 import torch
 
@@ -28,9 +29,11 @@ def test_two_stream_step_matches_one_stream():
     main = torch.cuda.current_stream(dev)
     side = torch.cuda.Stream(device=dev)      # default priority
 
-    def forward():
+    def forward_quantize():
         nv.nvfp4_quantize(x, axis=1, out=qx)
         nv.nvfp4_quantize(w, axis=1, out=qw)
+
+    def forward_gemm():
         nv.nvfp4_gemm(qx, qw, torch.bfloat16, out=y)
 
     def backward_operands():
@@ -47,7 +50,8 @@ def test_two_stream_step_matches_one_stream():
         return [t.clone() for t in (y, dx, dw, qx.codes, qw0.codes, qw0.scales, qw0.meta, qx0.codes, qx0.scales,
                                     qx0.meta, qdy.codes, qdyt.codes)]
 
-    forward()
+    forward_quantize()
+    forward_gemm()
     backward_operands()
     backward()
     torch.cuda.synchronize()
@@ -57,14 +61,15 @@ def test_two_stream_step_matches_one_stream():
     torch.cuda.synchronize()
 
     for _ in range(3):
-        start = torch.cuda.Event()
-        start.record(main)
-        side.wait_event(start)
+        forward_quantize()
+        release = torch.cuda.Event()
+        release.record(main)
+        side.wait_event(release)
         with torch.cuda.stream(side):
             backward_operands()
         done = torch.cuda.Event()
         done.record(side)
-        forward()
+        forward_gemm()
         main.wait_event(done)
         backward()
         torch.cuda.synchronize()
