@@ -14,8 +14,9 @@ W's axis-0 and X's axis-0 RHT quantizations (the backward operands of
 forward-time tensors) run on a second stream beside the fprop GEMM.
 value = GEMM FLOP of the step / step time (quantization included), TFLOP/s.
 Also reported: quantizer GB/s per operand and on the 32768x8192 sweep tensor
-(RNE/SR x RHT off/on), the fprop operands' quantization warm and after a
-512 MiB cache flush, per-GEMM TFLOP/s, the roofline of the dominant kernel
+(RNE/SR x RHT off/on) and its dequantize to bf16 and f32, the fprop operands'
+quantization warm and after a 512 MiB cache flush, per-GEMM TFLOP/s, the
+roofline of the dominant kernel
 (the f32-output GEMM that serves dgrad and wgrad), the same products in bf16
 and the same step in MXFP4 as context, and the CPU oracle timed on a bounded
 sample of the same step.
@@ -480,6 +481,7 @@ def main():
 
     # ------------------------------------------------ quantizer sweep ----
     sweep = None
+    dequant = None
     if not args.no_sweep:
         T = workloads.SWEEP.generate().to(dev)
         qT = nv.NVFP4Tensor.empty(32768, 8192)
@@ -509,6 +511,25 @@ def main():
                     gbs = b / (ms * 1e-3) / 1e9
                     sweep[f"axis{axis} {rnd}{'+rht' if rht else ''}"] = {
                         "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4)}
+        # dequantize of the same tensor (the last axis-1 result): codes and
+        # scales read once (0.5625 B/element), values written once
+        dequant = {}
+        for name, dt, eb in (("bf16", torch.bfloat16, 2), ("f32", torch.float32, 4)):
+            yq = torch.empty((32768, 8192), dtype=dt, device=dev)
+            for _ in range(2):
+                nv.nvfp4_dequantize(qT, dt, out=yq)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                nv.nvfp4_dequantize(qT, dt, out=yq)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            db = T.numel() * 9 // 16 + T.numel() * eb
+            dequant[name] = {"ms": round(ms, 4), "GB/s": round(db / (ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(db / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+            del yq
         del T, qT, qTt
 
     # ------------------------------- fprop operands, warm and cold ----
@@ -636,6 +657,7 @@ def main():
         "measured_peaks": measured_peaks,
         "breakdown": breakdown,
         "quantize_sweep_32768x8192_bf16": sweep,
+        "dequantize_32768x8192": dequant,
         "fprop_quantize_warm_vs_flushed": fprop_cache,
         "bf16_gemm_context": bf16_ctx,
         "mxfp4_step_context": mx_ctx,

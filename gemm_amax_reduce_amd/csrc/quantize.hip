@@ -367,10 +367,10 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
 
 // ---------------------------------------------------------- dequantize ----
 
-// One thread per 16-block: value = (e2m1 * S) * g, S applied exactly in f16.
-template <typename TO>
-__global__ void __launch_bounds__(kQT) k_dequant(const uint2 *codes, const uint8_t *scales, const float *meta,
-                                                int64_t nblocks, TO *y) {
+// bf16 output: one thread per 16-block (32 bytes of output in two 16-byte
+// stores); value = (e2m1 * S) * g in f32, rounded once to bf16.
+__global__ void __launch_bounds__(kQT) k_dequant_bf16(const uint2 *codes, const uint8_t *scales, const float *meta,
+                                                     int64_t nblocks, uint16_t *y) {
   const float g = meta[1];
   const int64_t stride = (int64_t)gridDim.x * kQT;
   for (int64_t b = (int64_t)blockIdx.x * kQT + threadIdx.x; b < nblocks; b += stride) {
@@ -387,24 +387,39 @@ __global__ void __launch_bounds__(kQT) k_dequant(const uint2 *codes, const uint8
         v[8 * h + j] = ((float)q[0] * S) * g;
       }
     }
-    if constexpr (sizeof(TO) == 4) {
-      float4 *dst = reinterpret_cast<float4 *>(y + 16 * b);
+    uint32_t o[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-    } else {
-      uint32_t o[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // nearest-even bf16 of each f32 (NaN cannot occur for finite meta)
-        uint32_t lo = __float_as_uint(v[2 * i]), hi = __float_as_uint(v[2 * i + 1]);
-        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
-        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-        o[i] = lo | (hi << 16);
-      }
-      uint4 *dst = reinterpret_cast<uint4 *>(y + 16 * b);
-      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    for (int i = 0; i < 8; ++i) {
+      // nearest-even bf16 of each f32 (NaN cannot occur for finite meta)
+      uint32_t lo = __float_as_uint(v[2 * i]), hi = __float_as_uint(v[2 * i + 1]);
+      lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+      hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+      o[i] = lo | (hi << 16);
     }
+    uint4 *dst = reinterpret_cast<uint4 *>(y + 16 * b);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// f32 output: one thread per quarter block (4 elements, one 16-byte store),
+// so the lanes of a wave store one contiguous 1 KB run per instruction (a
+// thread per block wrote 16-byte pieces 64 bytes apart: 32 % slower on a
+// 1 GiB output).  Same arithmetic as the bf16 kernel.
+__global__ void __launch_bounds__(kQT) k_dequant_f32(const uint16_t *codes, const uint8_t *scales, const float *meta,
+                                                    int64_t nquarters, float *y) {
+  const float g = meta[1];
+  const int64_t stride = (int64_t)gridDim.x * kQT;
+  for (int64_t q = (int64_t)blockIdx.x * kQT + threadIdx.x; q < nquarters; q += stride) {
+    const uint32_t w = codes[q];           // elements 4(q%4) .. +3 of block q/4: 2 code bytes
+    const float S = e4m3_to_f32(scales[q >> 2]);
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w >> (4 * j)) & 15u, 1.0f, 0);
+      v[j] = ((float)h[0] * S) * g;
+    }
+    *reinterpret_cast<float4 *>(y + 4 * q) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -704,11 +719,12 @@ hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const 
                              int64_t k, void *y, int y_dtype, hipStream_t stream) {
   const int64_t nblocks = outer * (k / 16);
   if (nblocks == 0) return hipSuccess;
-  unsigned g = grid_for(nblocks);
   if (y_dtype == 0)
-    hipLaunchKernelGGL(k_dequant<float>, dim3(g), dim3(kQT), 0, stream, (const uint2 *)codes, scales, meta, nblocks, (float *)y);
+    hipLaunchKernelGGL(k_dequant_f32, dim3(grid_for(4 * nblocks)), dim3(kQT), 0, stream, (const uint16_t *)codes,
+                       scales, meta, 4 * nblocks, (float *)y);
   else
-    hipLaunchKernelGGL(k_dequant<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint2 *)codes, scales, meta, nblocks, (uint16_t *)y);
+    hipLaunchKernelGGL(k_dequant_bf16, dim3(grid_for(nblocks)), dim3(kQT), 0, stream, (const uint2 *)codes, scales,
+                       meta, nblocks, (uint16_t *)y);
   return hipGetLastError();
 }
 
