@@ -153,6 +153,25 @@ def test_dequantize_bit_exact(out):
     np.testing.assert_array_equal(got.view(exp.dtype), exp)
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (4096, 5120)], ids=["1x16", "3x48", "4096x5120"])
+def test_dequantize_sizes(out, shape):
+    """One block, an odd number of blocks, and a layer-sized operand (grid
+    far above one round of the CUs), bit-exact against the oracle."""
+    nv = _nv()
+    rows, cols = shape
+    x = workloads.to_bf16(workloads.normal(rows, cols, 57 + rows))
+    ref = oracle.quantize(x, axis=1)
+    q = nv.NVFP4Tensor(torch.from_numpy(ref.codes).cuda(), torch.from_numpy(ref.scales).cuda(),
+                       torch.from_numpy(ref.meta).cuda(), ref.outer, ref.k)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = nv.nvfp4_dequantize(q, dt)
+    torch.cuda.synchronize()
+    exp = oracle.dequantize(ref, oracle.F32 if out == "f32" else oracle.BF16)
+    got = y.cpu().view(torch.int32 if out == "f32" else torch.int16).numpy()
+    np.testing.assert_array_equal(got.view(exp.dtype), exp)
+
+
 # ------------------------------------------------------ full workloads ----
 
 FULL = [
