@@ -31,23 +31,31 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# NVFP4_ORACLE_SANITIZE=1 selects a build instrumented with AddressSanitizer
+# and UndefinedBehaviorSanitizer (the process must preload gcc's libasan);
+# tests/test_oracle_sanitized.py runs the oracle pins that way.
+SANITIZE = os.environ.get("NVFP4_ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 F32, BF16 = 0, 1
 RNE, SR = 0, 1
 
 
-def build(force: bool = True) -> str:
-    """Compile ``liboracle.so`` with gcc (OpenMP, no FP contraction)."""
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off",
+def build(force: bool = True, sanitize: bool = SANITIZE) -> str:
+    """Compile the oracle's C code with gcc (OpenMP, no FP contraction) into
+    ``liboracle.so``, or with ``sanitize`` into ``liboracle_san.so`` with
+    AddressSanitizer and UndefinedBehaviorSanitizer (any finding aborts)."""
+    path = os.path.join(_HERE, "liboracle_san.so" if sanitize else "liboracle.so")
+    if not force and os.path.exists(path):
+        return path
+    tmp = path + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2" if not sanitize else "-O1", "-fopenmp", "-ffp-contract=off",
            "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp, _SRC, "-lm"]
+           *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, path)
+    return path
 
 
 _lib = None
