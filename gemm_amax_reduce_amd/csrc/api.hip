@@ -43,6 +43,23 @@ int check_tensor(const nvfp4_tensor *t) {
   return NVFP4_OK;
 }
 
+// Operands and output of an NVFP4 GEMM (shared by its entry points).
+int check_gemm_args(const nvfp4_tensor *a, const nvfp4_tensor *b, const void *c, int c_dtype, int64_t ldc) {
+  int st = check_tensor(a);
+  if (st != NVFP4_OK) return st;
+  st = check_tensor(b);
+  if (st != NVFP4_OK) return st;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (a->k != b->k) return NVFP4_ERR_SHAPE;
+  const int64_t M = a->outer, N = b->outer;
+  if (ldc < N || !count_ok(M, ldc) || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
+  if (M > 0 && N > 0 && !c) return NVFP4_ERR_NULL;
+  if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
+  // with K % 64 == 0 the kernels move the scale rows by DMA in whole dwords
+  if (a->k % 64 == 0 && (!aligned(a->scales, 4) || !aligned(b->scales, 4))) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
 int quantize_common(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rounding,
                     uint64_t seed, uint64_t offset, bool rht, uint32_t sign_mask, nvfp4_tensor *out,
                     void *hip_stream) {
@@ -133,7 +150,9 @@ int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   if (st != NVFP4_OK) return st;
   st = check_tensor(out0);
   if (st != NVFP4_OK) return st;
-  if (out1->meta == out0->meta) return NVFP4_ERR_SHAPE;   // the two maxima need their own words
+  // each meta is two floats that the kernels write while other workgroups
+  // read them: the two 8-byte ranges must not overlap
+  if (out1->meta + 2 > out0->meta && out0->meta + 2 > out1->meta) return NVFP4_ERR_SHAPE;
   if (!aligned(x, 16)) return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_quantize_dual(x, x_dtype, rows, cols, rounding1, seed1, offset1, out1->codes,
                                                 out1->scales, out1->meta, rht0 != 0, sign_mask0, rounding0, seed0,
@@ -184,21 +203,24 @@ int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stre
 }
 
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc, void *hip_stream) {
-  int st = check_tensor(a);
+  int st = check_gemm_args(a, b, c, c_dtype, ldc);
   if (st != NVFP4_OK) return st;
-  st = check_tensor(b);
-  if (st != NVFP4_OK) return st;
-  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
-  if (a->k != b->k) return NVFP4_ERR_SHAPE;
-  const int64_t M = a->outer, N = b->outer;
-  if (ldc < N || !count_ok(M, ldc) || !gemm_shape_ok(M, N, a->k)) return NVFP4_ERR_SHAPE;
-  if (M > 0 && N > 0 && !c) return NVFP4_ERR_NULL;
-  if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
-  // with K % 64 == 0 the kernel moves the scale rows by DMA in whole dwords
-  if (a->k % 64 == 0 && (!aligned(a->scales, 4) || !aligned(b->scales, 4))) return NVFP4_ERR_ALIGN;
-  return hip_status(nvfp4::launch_gemm(a->codes, a->scales, a->meta, b->codes, b->scales, b->meta, M, N, a->k, c,
+  return hip_status(nvfp4::launch_gemm(a->codes, a->scales, a->meta, b->codes, b->scales, b->meta, a->outer, b->outer, a->k, c,
                                        c_dtype, ldc, (hipStream_t)hip_stream));
 }
+
+int nvfp4_gemm_ws(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc, void *workspace,
+                  int64_t workspace_bytes, void *hip_stream) {
+  int st = check_gemm_args(a, b, c, c_dtype, ldc);
+  if (st != NVFP4_OK) return st;
+  if (!workspace) return NVFP4_ERR_NULL;
+  if (workspace_bytes < nvfp4::gemm_split_workspace_bytes()) return NVFP4_ERR_SHAPE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_gemm_split(a->codes, a->scales, a->meta, b->codes, b->scales, b->meta, a->outer,
+                                          b->outer, a->k, c, c_dtype, ldc, workspace, (hipStream_t)hip_stream));
+}
+
+int64_t nvfp4_gemm_workspace_bytes(void) { return nvfp4::gemm_split_workspace_bytes(); }
 
 const char *nvfp4_status_string(int status) {
   switch (status) {

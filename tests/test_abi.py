@@ -111,6 +111,22 @@ def test_binding_refuses_cpu_tensors():
 
 
 @_no_gpu
+def test_gemm_ws_argument_errors(L):
+    by = ctypes.byref
+    a, b = _t(64, 64), _t(32, 64)
+    need = L.nvfp4_gemm_workspace_bytes()
+    assert need == (64 << 10) + 256 * (256 << 10)
+    call = L.nvfp4_gemm_ws
+    assert call(None, by(b), FAKE, 0, 32, FAKE, need, None) == -1           # a NULL
+    assert call(by(a), by(b), FAKE, 0, 32, None, need, None) == -1          # workspace NULL
+    assert call(by(a), by(b), FAKE, 0, 32, FAKE, need - 1, None) == -2      # workspace too small
+    assert call(by(a), by(b), FAKE, 0, 32, FAKE + 16, need, None) == -5     # workspace misaligned
+    assert call(by(a), by(b), FAKE, 7, 32, FAKE, need, None) == -3          # dtype
+    assert call(by(a), by(b), FAKE, 0, 31, FAKE, need, None) == -2          # ldc < N
+    assert call(by(a), by(_t(32, 48)), FAKE, 0, 32, FAKE, need, None) == -2 # K mismatch
+
+
+@_no_gpu
 def test_quantize_dual_argument_errors(L):
     by = ctypes.byref
     q1, q0 = _t(16, 32), _t(32, 16, meta=FAKE + 64)
@@ -126,6 +142,10 @@ def test_quantize_dual_argument_errors(L):
     assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q0), 0, 0, 0, 0, 0, by(q1), None) == -2     # swapped outputs
     qsame = _t(32, 16)
     assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(qsame), None) == -2  # shared meta
+    # overlapping meta pairs: out0's {amax, g} one float after out1's, and before it
+    for m0 in (FAKE + 4, FAKE - 4):
+        qover = _t(32, 16, meta=m0)
+        assert call(FAKE, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(qover), None) == -2
     assert call(None, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -1     # x NULL
     assert call(FAKE + 2, 1, 16, 32, 0, 0, 0, by(q1), 0, 0, 0, 0, 0, by(q0), None) == -5 # x misaligned
 
