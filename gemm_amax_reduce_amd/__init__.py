@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_amax",
            "nvfp4_quantize_amax", "MXFP4Tensor", "mxfp4_quantize", "mxfp4_gemm",
-           "nvfp4_dequantize", "nvfp4_gemm", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
+           "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws", "gemm_workspace", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
@@ -44,8 +44,8 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_quantize_dual",
-           "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_probe_mfma",
-           "nvfp4_status_string")
+           "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws",
+           "nvfp4_gemm_workspace_bytes", "nvfp4_probe_mfma", "nvfp4_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_dequantize.restype = ci
         L.nvfp4_gemm.argtypes = [pt, pt, vp, ci, i64, vp]
         L.nvfp4_gemm.restype = ci
+        L.nvfp4_gemm_ws.argtypes = [pt, pt, vp, ci, i64, vp, i64, vp]
+        L.nvfp4_gemm_ws.restype = ci
+        L.nvfp4_gemm_workspace_bytes.argtypes = []
+        L.nvfp4_gemm_workspace_bytes.restype = i64
         L.nvfp4_probe_mfma.argtypes = [i64, vp, vp]
         L.nvfp4_probe_mfma.restype = ci
         L.nvfp4_status_string.argtypes = [ci]
@@ -318,6 +322,41 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: tor
     with torch.cuda.device(dev):
         _check(lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
                                 _stream_handle(stream, dev)), "nvfp4_gemm")
+    return out
+
+
+_workspaces: dict = {}
+
+
+def gemm_workspace(device=None) -> torch.Tensor:
+    """The stream-K GEMM workspace of `device` (allocated zero-filled on
+    first use and kept: the kernel leaves it zero-filled).  Calls that share
+    it must not overlap in time, so it serves one stream at a time."""
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    ws = _workspaces.get(device)
+    if ws is None:
+        ws = torch.zeros(int(lib().nvfp4_gemm_workspace_bytes()), dtype=torch.uint8, device=device)
+        _workspaces[device] = ws
+    return ws
+
+
+def nvfp4_gemm_ws(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C = A . B^T on the stream-K schedule (same result contract as
+    nvfp4_gemm); `workspace` defaults to the device's shared one."""
+    code = _out_code(out_dtype)
+    dev = a.device
+    if b.device != dev:
+        raise NVFP4Error(f"operands on {a.device} and {b.device}")
+    if out is None:
+        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=dev)
+    ldc = _require_matrix_out(out, a.outer, b.outer, out_dtype, dev)
+    ws = workspace if workspace is not None else gemm_workspace(dev)
+    _require_buffer(ws, "workspace", torch.uint8, int(lib().nvfp4_gemm_workspace_bytes()), dev)
+    ca, cb = a._c(), b._c()
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_gemm_ws(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc, ws.data_ptr(),
+                                   ws.numel(), _stream_handle(stream, dev)), "nvfp4_gemm_ws")
     return out
 
 

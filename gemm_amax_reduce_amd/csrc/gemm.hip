@@ -13,8 +13,10 @@
 // elements, so every element is decoded exactly: the hardware FP4->F16
 // conversion gives q and one packed f16 multiply by the block scale gives
 // q*S.  q*S has at most 6 significant bits and lies in [2^-10, 2688], so it
-// is exact in f16, and every 16-element partial sum of the f16 MFMA is exact
-// in f32.
+// is exact in f16 and every product of two is exact in f32.  One MFMA sums a
+// K step of 16 products taken from two different 16-blocks (8 positions of
+// each, see the K order below) into the f32 accumulator, so the rounding is
+// that of about K/16 binary32 accumulations.
 //
 // Data movement.  A 256-thread workgroup computes a 256 x BN tile of C (BN =
 // 256, or 128 for the column remainder) with four waves of 128 x BN/2.  K is
@@ -68,14 +70,20 @@ constexpr int kGroupM = 8;                          // tile rows per L2 group
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// One 256 x BN output tile: workgroup `pid` of the tiles of C[M][N] = A.B^T
-// (B, C and N already restricted to this tile width's column range).
-template <bool OUT_BF16, bool SCALE_DMA, int BN>
-__device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t *__restrict__ A,
-                                          const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
-                                          const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
-                                          const float *__restrict__ metaB, int64_t M, int64_t N, int64_t K,
-                                          void *__restrict__ C, int64_t ldc) {
+// The f32 accumulators of one 256 x BN tile: wave (wm, wn) holds rows
+// 128wm + 32i and columns (BN/2)wn + 32j of MFMA block [i][j].
+template <int BN> using TileAcc = float16_t[4][BN / 64];
+
+// acc = the unscaled sum over K groups [g0, g1) of the 256 x BN tile of
+// C[M][N] = A.B^T at rows m0.., columns n0.. (B, N already restricted to
+// this tile width's column range).  g1 > g0.  Every DMA this issues has
+// completed when it returns, so the LDS buffers are free again once all
+// waves are past a barrier.
+template <bool SCALE_DMA, int BN>
+__device__ __forceinline__ void tile_accumulate(uint8_t *smem, int64_t m0, int64_t n0, int g0, int g1,
+                                                const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
+                                                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                                                int64_t M, int64_t N, int64_t K, TileAcc<BN> &acc) {
   constexpr int NB = BN / 64;          // B fragments (32 columns each) per wave
   constexpr int NF = 4 + NB;           // operand fragments decoded per wave and K step
   constexpr int NU = 4 * NB;           // MFMAs per wave and K step
@@ -86,12 +94,6 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   // compiler so, which keeps every per-wave choice in scalar registers.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
-
-  // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
-  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  int tm, tn;
-  xcd_tile(pid, tiles_m, tiles_n, kGroupM, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   // ---- DMA side: waves 0 and 1 copy A rows 128w .. 128w+127, waves 2 and
   // 3 B rows kRowsB(w-2) ..; a view holds only rows inside the operand, so
@@ -114,7 +116,6 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   // holds the row's chunk (l&7) ^ (row&7)
   const uint32_t dv_code = (uint32_t)(lane >> 3) * rb + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
   const uint32_t dv_scale = (uint32_t)lane * rs;     // scale DMA: 64 rows, lane l -> row l
-  const int ng = (int)((K + kGroupK - 1) / kGroupK);
   // Part `part` of the DMA of group g into LDS buffer buf.  The 16 code and
   // 2 scale instructions of a group are spread over four stages (parts 3,
   // 0, 1, 2 in issue order: code instructions 0-4, 5-9, 10-14, then 15 and
@@ -123,7 +124,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   // DMA of the prefetch distance needs no branch at the end of K.
   auto dma_part = [&](int g, int buf, int part) {
     uint8_t *gbuf = smem + buf * kGroupBytes;
-    const bool gin = g < ng;
+    const bool gin = g < g1;
     const int q0 = part == 3 ? 0 : 5 * part + 5, q1 = part == 3 ? 5 : part == 2 ? 16 : q0 + 5;
 #pragma unroll
     for (int qq = q0; qq < q1; ++qq) {
@@ -162,7 +163,6 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   uint32_t keep = 0;       // which of those two scales lie inside K
   half2_t spair[NF];       // ... as an f16 pair
   half8_t opnd[2][NF];     // [K step parity][fragment]: decoded MFMA operands
-  float16_t acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -238,14 +238,15 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
     d[4 * part + 3] = x1[1];
   };
 
-  // ---- prologue: group 0 and the first part of group 1 in flight (the
-  // rest of group 1 follows in stages 0-2), stage 0 read, K step 0 decoded
+  // ---- prologue: group g0 and the first part of group g0+1 in flight
+  // (the rest of group g0+1 follows in stages 0-2), stage 0 read, K step 0
+  // decoded.  Group g lives in LDS buffer g & 1.
 #pragma unroll
-  for (int part = 0; part < 4; ++part) dma_part(0, 0, part);
-  dma_part(1, 1, 3);
+  for (int part = 0; part < 4; ++part) dma_part(g0, g0 & 1, part);
+  dma_part(g0 + 1, (g0 + 1) & 1, 3);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  read_stage(0, smem, 0, 0);
+  read_stage(0, smem + (g0 & 1) * kGroupBytes, g0, 0);
   __builtin_amdgcn_s_waitcnt(0);     // nothing outstanding at loop entry
   if constexpr (SCALE_DMA) pick_scales();
   scale_pairs(std::integral_constant<int, 0>{});
@@ -311,18 +312,26 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
   using P3 = std::integral_constant<int, 3>;
-  for (int g = 0; g < ng; ++g) {
+  for (int g = g0; g < g1; ++g) {
     stage(g, P0{});
     stage(g, P1{});
     stage(g, P2{});
     stage(g, P3{});
   }
   __builtin_amdgcn_sched_barrier(0);
+  // the prefetch DMAs past g1 (out of range) are the only ones left
+  __builtin_amdgcn_s_waitcnt(0);
+}
 
-  // ---- epilogue: C = (acc * gA) * gB.  Lane holds column r and rows
-  // 8*(e/4) + 4*h + e%4 of each 32x32 tile; row offsets are uniform, so the
-  // per-store address is one lane base plus a scalar offset.
-  const float gA = metaA[1], gB = metaB[1];
+// C tile = (acc * gA) * gB.  Lane holds column r and rows 8*(e/4) + 4*h +
+// e%4 of each 32x32 block; row offsets are uniform, so the per-store address
+// is one lane base plus a scalar offset.
+template <bool OUT_BF16, int BN>
+__device__ __forceinline__ void tile_store(const TileAcc<BN> &acc, int64_t m0, int64_t n0, float gA, float gB,
+                                           int64_t M, int64_t N, void *__restrict__ C, int64_t ldc) {
+  constexpr int NB = BN / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
   const int64_t row_l = m0 + wm * 128 + 4 * h, col_l = n0 + wn * (BN / 2) + r;
   const bool full_tile = (m0 + BM <= M) && (n0 + BN <= N);
   using OutT = typename std::conditional<OUT_BF16, uint16_t, float>::type;
@@ -347,6 +356,24 @@ __device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t 
   }
 }
 
+// One 256 x BN output tile: workgroup `pid` of the tiles of C[M][N] = A.B^T
+// (B, C and N already restricted to this tile width's column range), placed
+// XCD-contiguously and grouped by tile rows.
+template <bool OUT_BF16, bool SCALE_DMA, int BN>
+__device__ __forceinline__ void gemm_tile(uint8_t *smem, int pid, const uint8_t *__restrict__ A,
+                                          const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
+                                          const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                                          const float *__restrict__ metaB, int64_t M, int64_t N, int64_t K,
+                                          void *__restrict__ C, int64_t ldc) {
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  int tm, tn;
+  xcd_tile(pid, tiles_m, tiles_n, kGroupM, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  TileAcc<BN> acc;
+  tile_accumulate<SCALE_DMA, BN>(smem, m0, n0, 0, (int)((K + kGroupK - 1) / kGroupK), A, SA, B, SB, M, N, K, acc);
+  tile_store<OUT_BF16, BN>(acc, m0, n0, metaA[1], metaB[1], M, N, C, ldc);
+}
+
 // The GEMM kernel: workgroups [0, n_big) compute the 256 x 256 tiles of
 // columns [0, n1), the others the 256 x 128 tiles of columns [n1, N).  The
 // branch is uniform per workgroup; LDS holds two group buffers sized for the
@@ -365,6 +392,166 @@ k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
     gemm_tile<OUT_BF16, SCALE_DMA, 128>(smem, pid - n_big, A, SA, metaA, B + n1 * (K / 2), SB + n1 * (K / 16), metaB, M,
                              N - n1, K, reinterpret_cast<OutT *>(C) + n1, ldc);
   }
+}
+
+// ------------------------------------------------------- split tail ----
+//
+// The data-parallel grid runs whole tiles, so when the tile count is not a
+// multiple of the CU count the last round leaves CUs idle (the layer shapes
+// have 320, 640 and 1600 tiles of 256 x 256 on 256 CUs: 1.25, 2.5 and 6.25
+// rounds).  Here the whole rounds run as before, and each of the remaining
+// `rem` tiles is cut into `sp` equal K ranges (sp = CUs / rem, at least
+// kMinSplitGroups K groups per range), one workgroup per range, so the last
+// round fills the CUs: 20 + 5, 2 x 80 + 40 and 6 x 32 + 8 group-times for
+// the three layers against 40, 240 and 224 with whole tiles.
+//
+// Of the sp workgroups of a split tile, the last (highest-numbered) one
+// finishes it: the others each write their unscaled f32 partial to their
+// own workspace slot and raise its flag; the finisher waits for the flags,
+// adds the partials in increasing range order to its own, and stores the
+// tile.  The result does not depend on timing (deterministic).  Splitting
+// pays only where the tail's ranges are long or most CUs would otherwise
+// idle: measured on the layer shapes, dgrad (a 2-way split of 40-group
+// ranges) gains 1.5 %, while the 4-way splits of 5- and 8-group ranges of
+// fprop and wgrad lose 10 % and 1 % to the mixed 256/128-wide grid (a
+// second wave of short workgroups, each with its own prologue, partial and
+// wait), so the launcher takes that grid there.
+//
+// Progress: a finisher waits only for lower-numbered workgroups, which never
+// wait themselves; workgroups of one dispatch start in increasing order (per
+// XCD), so every wait ends.  The wait is bounded anyway: after about a
+// second it gives up, counts the event in the workspace's error word and
+// finishes the tile (that output is then wrong, but the kernel drains).
+//
+// Workspace: flags at bytes [0, 32 KB) (slot t's at 128 t), the error word
+// at 32 KB, slot t's partial (256 x 256 f32, 256 KB) at 64 KB + 256 KB t.
+// Flags are 0 between launches: the finisher clears each flag it consumed.
+constexpr int kSplitMaxSlots = 256;
+constexpr int64_t kSplitFlagBytes = 128;
+constexpr int64_t kSplitErrOffset = 32 << 10;
+constexpr int64_t kSplitSlot0 = 64 << 10;
+constexpr int64_t kSplitSlotBytes = (int64_t)BM * 256 * 4;
+constexpr unsigned kSplitSpinLimit = 1u << 20;        // polls of ~1000 clocks each
+
+struct SplitSched {
+  int tiles_m, tiles_n;     // 256 x 256 tiles of C, in row groups of kGroupM
+  int n_dp;                 // whole tiles (the first n_dp in that order), one workgroup each
+  int sp;                   // K ranges per remaining tile (1: no split)
+};
+
+// Tile u (0 .. tiles-1) in row groups of kGroupM tile rows.
+__device__ __forceinline__ void grouped_tile(int u, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (u / per_group) * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  tm = first_m + (u % per_group) % gsz;
+  tn = (u % per_group) / gsz;
+}
+
+// Workgroup pid of n (dealt round-robin to the eight XCDs) -> its index in
+// an XCD-contiguous order of n items.
+__device__ __forceinline__ int xcd_logical(int pid, int n) {
+  constexpr int kXcds = 8;
+  const int xcd = pid % kXcds, local = pid / kXcds;
+  const int q = n / kXcds, rq = n % kXcds;
+  return (xcd < rq) ? xcd * (q + 1) + local : rq * (q + 1) + (xcd - rq) * q + local;
+}
+
+template <bool OUT_BF16, bool SCALE_DMA>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_gemm_nvfp4_split(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
+                   const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
+                   int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc, uint8_t *__restrict__ ws,
+                   SplitSched sc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kGroupBytes];
+  const int pid = blockIdx.x, tid = threadIdx.x;
+  const int ng = (int)((K + kGroupK - 1) / kGroupK);
+  int u, g0 = 0, g1 = ng, part = 0, t = 0;
+  if (pid < sc.n_dp) {
+    u = xcd_logical(pid, sc.n_dp);
+  } else {
+    t = pid - sc.n_dp;
+    part = t % sc.sp;
+    u = sc.n_dp + t / sc.sp;
+    g0 = (int)((int64_t)part * ng / sc.sp);
+    g1 = (int)((int64_t)(part + 1) * ng / sc.sp);
+  }
+  int tm, tn;
+  grouped_tile(u, sc.tiles_m, sc.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 256;
+  TileAcc<256> acc;
+  tile_accumulate<SCALE_DMA, 256>(smem, m0, n0, g0, g1, A, SA, B, SB, M, N, K, acc);
+  // Partial slot t holds float4 q of thread tid at byte 16 * (256 q + tid),
+  // so each wave's store or load instruction covers one contiguous
+  // kilobyte.  Partials are written and read with device-scope coherence
+  // (the sc1 cache policy: the stores write through this XCD's L2, the
+  // loads do not hit stale lines in the reader's), which makes them visible
+  // across XCDs once the stores have completed; the flag follows after
+  // the wait for completion.  (A release fence instead writes back the
+  // whole L2 of the XCD: measured 25 us slower on the fprop layer.)
+  constexpr int kDeviceScope = 0x10;     // cache-policy bits: sc1
+  const __amdgpu_buffer_rsrc_t slot = make_rsrc(ws + kSplitSlot0 + (int64_t)t * kSplitSlotBytes, (uint32_t)kSplitSlotBytes);
+  if (pid >= sc.n_dp && part < sc.sp - 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              (u32x4){__float_as_uint(acc[i][j][4 * c]), __float_as_uint(acc[i][j][4 * c + 1]),
+                      __float_as_uint(acc[i][j][4 * c + 2]), __float_as_uint(acc[i][j][4 * c + 3])},
+              slot, (uint32_t)(16 * (256 * ((i * 4 + j) * 4 + c) + tid)), 0, kDeviceScope);
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's partial stores have completed
+    __syncthreads();                   // ... and every other wave's
+    if (tid == 0)
+      __hip_atomic_store(reinterpret_cast<unsigned *>(ws + (int64_t)t * kSplitFlagBytes), 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (pid >= sc.n_dp && sc.sp > 1) {
+    // the finisher: wait for ranges 0 .. sp-2 (slots t-part .. t-1), then
+    // add their partials one 32 x 32 block at a time (only that block's 16
+    // accumulators pass through the loop over contributors)
+    const int c0 = t - part;
+    if (tid == 0) {
+      for (int c = c0; c < t; ++c) {
+        unsigned *flag = reinterpret_cast<unsigned *>(ws + (int64_t)c * kSplitFlagBytes);
+        unsigned n = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+          if (++n >= kSplitSpinLimit) {
+            atomicAdd(reinterpret_cast<unsigned *>(ws + kSplitErrOffset), 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+        __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t parts =
+        make_rsrc(ws + kSplitSlot0 + (int64_t)c0 * kSplitSlotBytes, (uint32_t)(part * kSplitSlotBytes));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float16_t v = acc[i][j];
+        for (int c = 0; c < part; ++c) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(
+                parts, (uint32_t)(16 * (256 * ((i * 4 + j) * 4 + q) + tid)), (uint32_t)(c * kSplitSlotBytes),
+                kDeviceScope);
+            v[4 * q] += __uint_as_float(p.x);
+            v[4 * q + 1] += __uint_as_float(p.y);
+            v[4 * q + 2] += __uint_as_float(p.z);
+            v[4 * q + 3] += __uint_as_float(p.w);
+          }
+        }
+        acc[i][j] = v;
+      }
+  }
+  tile_store<OUT_BF16, 256>(acc, m0, n0, metaA[1], metaB[1], M, N, C, ldc);
 }
 
 __global__ void k_zero_c(void *C, int64_t M, int64_t N, int64_t ldc, int elem) {
@@ -442,6 +629,54 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
     else NVFP4_GEMM_LAUNCH(true, false);
   }
 #undef NVFP4_GEMM_LAUNCH
+  return hipGetLastError();
+}
+
+int64_t gemm_split_workspace_bytes() { return kSplitSlot0 + (int64_t)kSplitMaxSlots * kSplitSlotBytes; }
+
+hipError_t launch_gemm_split(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_meta,
+                          const uint8_t *b_codes, const uint8_t *b_scales, const float *b_meta, int64_t M,
+                          int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, void *ws, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K == 0) {
+    int64_t total = M * N;
+    unsigned g = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_zero_c, dim3(g), dim3(256), 0, stream, c, M, N, ldc, c_dtype == 0 ? 4 : 2);
+    return hipGetLastError();
+  }
+  if ((int64_t)128 * (K / 2) >= (int64_t)kOutOfRange) return hipErrorInvalidValue;
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + 255) / 256, tiles = tiles_m * tiles_n;
+  const int64_t ng = (K + kGroupK - 1) / kGroupK;
+  const int64_t P = std::min<int64_t>(device_cus(), kSplitMaxSlots);
+  // whole rounds data-parallel; the rem remaining tiles split into sp K
+  // ranges each, sp * rem <= P, at least kMinSplitGroups groups per range.
+  // The split is taken when most CUs would idle without it (fewer than P/2
+  // tiles) or when its ranges are long (at least kLongRangeGroups groups);
+  // otherwise the mixed-width data-parallel grid of launch_gemm is faster.
+  constexpr int64_t kMinSplitGroups = 4, kLongRangeGroups = 16;
+  const int64_t rem = tiles % P;
+  const int64_t sp = rem == 0 ? 1 : std::max<int64_t>(1, std::min<int64_t>(P / rem, ng / kMinSplitGroups));
+  if (sp == 1 || (2 * tiles >= P && ng / sp < kLongRangeGroups))
+    return launch_gemm(a_codes, a_scales, a_meta, b_codes, b_scales, b_meta, M, N, K, c, c_dtype, ldc, stream);
+  const int64_t grid = (tiles - rem) + rem * sp;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  SplitSched sc;
+  sc.tiles_m = (int)tiles_m;
+  sc.tiles_n = (int)tiles_n;
+  sc.n_dp = (int)(tiles - rem);
+  sc.sp = (int)sp;
+  const bool scale_dma = K % 64 == 0;
+#define NVFP4_GEMM_SPLIT_LAUNCH(OB, SD)                                                                         \
+  hipLaunchKernelGGL((k_gemm_nvfp4_split<OB, SD>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a_codes,     \
+                     a_scales, a_meta, b_codes, b_scales, b_meta, M, N, K, c, ldc, (uint8_t *)ws, sc)
+  if (c_dtype == 0) {
+    if (scale_dma) NVFP4_GEMM_SPLIT_LAUNCH(false, true);
+    else NVFP4_GEMM_SPLIT_LAUNCH(false, false);
+  } else {
+    if (scale_dma) NVFP4_GEMM_SPLIT_LAUNCH(true, true);
+    else NVFP4_GEMM_SPLIT_LAUNCH(true, false);
+  }
+#undef NVFP4_GEMM_SPLIT_LAUNCH
   return hipGetLastError();
 }
 

@@ -51,4 +51,14 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
                        const uint8_t *b_codes, const uint8_t *b_scales, const float *b_meta, int64_t M,
                        int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, hipStream_t stream);
 
+// The same product with the tiles left over after whole rounds of the CUs
+// cut into K ranges (split tail), where that is faster; split tiles are
+// combined in a fixed order through ws.  ws: gemm_split_workspace_bytes()
+// bytes, 256-byte aligned, zero-filled before its first use; left
+// zero-filled on completion.
+int64_t gemm_split_workspace_bytes();
+hipError_t launch_gemm_split(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_meta,
+                          const uint8_t *b_codes, const uint8_t *b_scales, const float *b_meta, int64_t M,
+                          int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, void *ws, hipStream_t stream);
+
 }  // namespace nvfp4

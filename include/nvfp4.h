@@ -34,7 +34,8 @@
  *    (rows * cols, outer * k, M * ldc) is at most 2^60.
  *  - Element types: NVFP4_F32 (binary32) or NVFP4_BF16 (bfloat16).
  *  - Thread safety: stateless; concurrent calls on different outputs are
- *    fine.  The calls keep no scratch memory between launches.
+ *    fine.  The calls keep no scratch memory between launches (the one
+ *    workspace, of nvfp4_gemm_ws, belongs to the caller).
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -169,8 +170,8 @@ int nvfp4_quantize_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, 
  * both maxima (the plain one, and the one after the column transform), the
  * encode pass writes both outputs from one tile of x staged in LDS.
  *  rows % 16 == 0 and cols % 16 == 0 (both layouts need whole blocks);
- *  out1: outer = rows, k = cols; out0: outer = cols, k = rows; out1->meta and
- *  out0->meta must be different words (NVFP4_ERR_SHAPE otherwise) and the
+ *  out1: outer = rows, k = cols; out0: outer = cols, k = rows; the two meta
+ *  pairs (8 bytes each) must not overlap (NVFP4_ERR_SHAPE otherwise) and the
  *  outputs must not overlap each other or x.  Enqueues three kernels.
  */
 int nvfp4_quantize_dual(const void *x, int x_dtype, int64_t rows, int64_t cols,
@@ -201,14 +202,58 @@ int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stre
  *      b = dY (axis 0).
  *  c : device, row-major [M][ldc], c_dtype NVFP4_F32 or NVFP4_BF16 (nearest
  *      even of the f32 result), ldc >= N, 4-byte aligned (f32) / 2-byte (bf16).
- * Accuracy: every element within 1e-5 * g_A g_B sum_k |(qA SA)(qB SB)| of the
- * exact value (each 16-element partial product sum is exact in f32; the
- * accumulation rounds once per 16-block step).  Deterministic: one kernel,
- * no atomics, fixed summation order.  M == 0 or N == 0: nothing is written;
- * K == 0: C is set to zero.
+ * Accuracy: every decoded element q*S is exact in f16 and every product of
+ * two is exact in f32.  Each MFMA adds one K step of 16 products -- 8 from
+ * each of two different 16-blocks, with different block scales -- into the
+ * f32 accumulator, so an output element goes through at least K/16 binary32
+ * roundings and the worst-case error is of order
+ * (K/16) * 2^-24 * g_A g_B sum_k |(qA SA)(qB SB)|: that guarantees the
+ * 1e-5 * sum|ab| tolerance only up to K of about 2700.  Beyond, the
+ * tolerance rests on successive rounding errors having independent signs
+ * (error ~ sqrt(K/16) * 2^-24 * sum|ab|).  Measured worst |err| / sum|ab|:
+ * zero-mean operands at the layer shapes (K = 5120 .. 20480) below 1e-6;
+ * non-negative operands (the case where every partial sum grows) 2.5e-6 at
+ * K = 20480, 6.9e-6 at K = 131072, and above the tolerance from K = 262144
+ * (1.04e-5; 1.9e-4 at K = 2^25 - 256).  So for same-sign operands this call
+ * meets 1e-5 for K <= 131072; nvfp4_gemm_ws splits long reductions of small
+ * outputs (3.5e-7 at K = 2^25 - 256).
+ * Deterministic: one kernel, no atomics, fixed summation order.  M == 0 or
+ * N == 0: nothing is written; K == 0: C is set to zero.
  */
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
                int64_t ldc, void *hip_stream);
+
+/*
+ * nvfp4_gemm_ws -- nvfp4_gemm with a caller-owned workspace, which lets it
+ * split the tiles of the last, partly filled round of the CUs into K ranges
+ * (split tail).  The data-parallel grid runs whole 256 x 256 output tiles,
+ * so when the tile count is not a multiple of the CU count the last round
+ * leaves CUs idle.  Here whole rounds run as before and each remaining tile
+ * is cut into up to CUs / tiles-left-over K ranges, one workgroup each; the
+ * workgroup of the last range adds the others' f32 partials (kept in the
+ * workspace) in a fixed order -- deterministic, no atomics on the data.
+ * The split is taken where it is faster: when fewer than half the CUs would
+ * get a tile, or when the ranges stay long (at least 4096 K positions);
+ * otherwise the call runs nvfp4_gemm's grid.  Same operands, output and
+ * accuracy contract as nvfp4_gemm; a split shortens each f32 accumulation
+ * chain (the partials then add in binary32), which keeps same-sign
+ * operands inside the tolerance at any K when the output has few tiles.
+ *  workspace       : device, at least nvfp4_gemm_workspace_bytes() bytes,
+ *                    256-byte aligned, zero-filled before its FIRST use (the
+ *                    kernel leaves it zero-filled again when it completes,
+ *                    so it can be reused without clearing).  Calls that use
+ *                    one workspace must not overlap in time (same stream,
+ *                    or ordered by events).
+ *  workspace_bytes : its size (NVFP4_ERR_SHAPE if smaller).
+ * Errors as nvfp4_gemm, plus NVFP4_ERR_NULL for a NULL workspace and
+ * NVFP4_ERR_ALIGN for a misaligned one.  Enqueues one kernel.
+ */
+int nvfp4_gemm_ws(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
+                  int64_t ldc, void *workspace, int64_t workspace_bytes, void *hip_stream);
+
+/* Workspace bytes nvfp4_gemm_ws needs (the same for every shape: 64 KiB of
+ * flags plus one 256 KiB partial per persistent workgroup, at most 256). */
+int64_t nvfp4_gemm_workspace_bytes(void);
 
 /*
  * MXFP4 -- the microscaling format the pages set NVFP4 against ([P4]
