@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_amax",
            "nvfp4_quantize_amax", "MXFP4Tensor", "mxfp4_quantize", "mxfp4_gemm",
-           "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws", "gemm_workspace", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
+           "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws", "nvfp4_gemm_noalloc", "gemm_workspace", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
@@ -45,7 +45,7 @@ _lib = None
 # every symbol the header declares
 EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_quantize_dual",
            "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws",
-           "nvfp4_gemm_workspace_bytes", "nvfp4_probe_mfma", "nvfp4_status_string")
+           "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_noalloc", "nvfp4_probe_mfma", "nvfp4_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemm_ws.argtypes = [pt, pt, vp, ci, i64, vp, i64, vp]
         L.nvfp4_gemm_ws.restype = ci
         L.nvfp4_gemm_workspace_bytes.argtypes = []
+        L.nvfp4_gemm_noalloc.argtypes = [pt, pt, vp, ci, i64, vp]
+        L.nvfp4_gemm_noalloc.restype = ci
         L.nvfp4_gemm_workspace_bytes.restype = i64
         L.nvfp4_probe_mfma.argtypes = [i64, vp, vp]
         L.nvfp4_probe_mfma.restype = ci
@@ -357,6 +359,23 @@ def nvfp4_gemm_ws(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: 
     with torch.cuda.device(dev):
         _check(lib().nvfp4_gemm_ws(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc, ws.data_ptr(),
                                    ws.numel(), _stream_handle(stream, dev)), "nvfp4_gemm_ws")
+    return out
+
+
+def nvfp4_gemm_noalloc(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor, out_dtype=torch.float32,
+                       stream=None) -> torch.Tensor:
+    """nvfp4_gemm_ws with the library's own per-GPU workspace: allocates
+    nothing (the caller supplies `out`).  Calls overlapping in time on one
+    GPU race."""
+    code = _out_code(out_dtype)
+    dev = a.device
+    if b.device != dev:
+        raise NVFP4Error(f"operands on {a.device} and {b.device}")
+    ldc = _require_matrix_out(out, a.outer, b.outer, out_dtype, dev)
+    ca, cb = a._c(), b._c()
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_gemm_noalloc(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
+                                        _stream_handle(stream, dev)), "nvfp4_gemm_noalloc")
     return out
 
 

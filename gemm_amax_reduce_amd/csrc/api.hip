@@ -222,6 +222,20 @@ int nvfp4_gemm_ws(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_d
 
 int64_t nvfp4_gemm_workspace_bytes(void) { return nvfp4::gemm_split_workspace_bytes(); }
 
+int nvfp4_gemm_noalloc(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype, int64_t ldc,
+                       void *hip_stream) {
+  int st = check_gemm_args(a, b, c, c_dtype, ldc);
+  if (st != NVFP4_OK) return st;
+  // the split launcher needs at most gemm_split_workspace_bytes() for any
+  // shape; beyond the library's array the call is refused
+  if (nvfp4::gemm_split_workspace_bytes() > nvfp4::gemm_scratch_bytes()) return NVFP4_ERR_SHAPE;
+  void *ws = nullptr;
+  hipError_t e = nvfp4::gemm_scratch((hipStream_t)hip_stream, &ws);
+  if (e != hipSuccess) return NVFP4_ERR_HIP;
+  return hip_status(nvfp4::launch_gemm_split(a->codes, a->scales, a->meta, b->codes, b->scales, b->meta, a->outer,
+                                             b->outer, a->k, c, c_dtype, ldc, ws, (hipStream_t)hip_stream));
+}
+
 const char *nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

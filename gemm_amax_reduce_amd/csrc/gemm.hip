@@ -634,6 +634,48 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
 
 int64_t gemm_split_workspace_bytes() { return kSplitSlot0 + (int64_t)kSplitMaxSlots * kSplitSlotBytes; }
 
+// ------------------------------------------- library-owned workspace ----
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops, harnesses that forbid it): the split GEMM's workspace as a
+// file-scope device array, one copy per GPU, held until the process ends.
+// In host code `scratch` names a host-side stand-in, so its device address
+// comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is passed to kernels.  Calls on one GPU
+// share the array: calls that overlap in time on one GPU race.
+constexpr int64_t kScratchBytes = kSplitSlot0 + (int64_t)kSplitMaxSlots * kSplitSlotBytes;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void k_zero_words(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+int64_t gemm_scratch_bytes() { return kScratchBytes; }
+
+hipError_t gemm_scratch(hipStream_t stream, void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // The flags and the error word must start at zero; the kernel leaves
+    // them at zero after every complete launch.  A fill kernel, ordered on
+    // the caller's stream before the first GEMM (no memset: it may be
+    // captured into a graph).
+    hipLaunchKernelGGL(k_zero_words, dim3(64), dim3(256), 0, stream, (uint32_t *)p, kSplitSlot0 / 4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t launch_gemm_split(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_meta,
                           const uint8_t *b_codes, const uint8_t *b_scales, const float *b_meta, int64_t M,
                           int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, void *ws, hipStream_t stream) {

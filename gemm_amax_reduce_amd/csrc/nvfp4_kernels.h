@@ -57,6 +57,11 @@ hipError_t launch_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const fl
 // bytes, 256-byte aligned, zero-filled before its first use; left
 // zero-filled on completion.
 int64_t gemm_split_workspace_bytes();
+// The library-owned workspace of the current device (set up on the first
+// call per device, its flags cleared by a kernel on `stream`), for the
+// entry point that allocates nothing; gemm_scratch_bytes() bytes.
+int64_t gemm_scratch_bytes();
+hipError_t gemm_scratch(hipStream_t stream, void **ptr);
 hipError_t launch_gemm_split(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_meta,
                           const uint8_t *b_codes, const uint8_t *b_scales, const float *b_meta, int64_t M,
                           int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, void *ws, hipStream_t stream);

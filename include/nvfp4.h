@@ -251,6 +251,23 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
 int nvfp4_gemm_ws(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
                   int64_t ldc, void *workspace, int64_t workspace_bytes, void *hip_stream);
 
+/*
+ * nvfp4_gemm_noalloc -- nvfp4_gemm_ws with the library's own workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  It allocates
+ * nothing: the workspace is a file-scope device array of
+ * nvfp4_gemm_workspace_bytes() bytes (64 MiB + 64 KiB), one per GPU the
+ * library runs on, held until the process ends; its address is looked up
+ * and its flags cleared (by a kernel on hip_stream) on the first call on
+ * each device.  Same arguments, results and errors as nvfp4_gemm_ws without
+ * the workspace; the output is bit-identical to nvfp4_gemm_ws's.  Every
+ * call on one GPU shares that array, so calls that overlap in time on one
+ * GPU race (use one stream, or order them); it keeps the last call's
+ * partials.  Enqueues one kernel (two on the first call on a device).
+ */
+int nvfp4_gemm_noalloc(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
+                       int64_t ldc, void *hip_stream);
+
 /* Workspace bytes nvfp4_gemm_ws needs (the same for every shape: 64 KiB of
  * flags plus one 256 KiB partial per persistent workgroup, at most 256). */
 int64_t nvfp4_gemm_workspace_bytes(void);
