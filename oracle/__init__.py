@@ -98,6 +98,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_mxfp4_quantize.restype = ctypes.c_int
         L.oracle_mxfp4_decode.argtypes = [vp, vp, c_i64, vp, c_i64, vp]
         L.oracle_mxfp4_decode.restype = ctypes.c_int
+        L.oracle_mx8_scale_exp.argtypes = [c_u32]
+        L.oracle_mx8_scale_exp.restype = ctypes.c_int
+        L.oracle_mxfp8_quantize.argtypes = [vp, ctypes.c_int, c_i64, c_i64, ctypes.c_int, vp, vp]
+        L.oracle_mxfp8_quantize.restype = ctypes.c_int
+        L.oracle_mxfp8_decode.argtypes = [vp, vp, c_i64, vp, c_i64, vp]
+        L.oracle_mxfp8_decode.restype = ctypes.c_int
+        L.oracle_mxfp8_trunc_bound.argtypes = [vp, vp, vp, vp, c_i64, vp, c_i64, vp, c_i64, vp]
+        L.oracle_mxfp8_trunc_bound.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -348,3 +356,87 @@ def mxfp4_gemm(qa: MXQuantized, qb: MXQuantized, rows=None, cols=None):
     db = mxfp4_decode(qb, cols)
     return da @ db.T, np.abs(da) @ np.abs(db).T
 
+
+
+# --------------------------------------------------------------- MXFP8 ----
+
+class MX8Quantized:
+    """An MXFP8 tensor in its quantized [outer][k] layout: codes u8
+    [outer, k] (OCP E4M3FN), scales u8 [outer, k/32] (E8M0: 2^(code - 127))."""
+
+    def __init__(self, codes, scales, outer, k):
+        self.codes, self.scales, self.outer, self.k = codes, scales, outer, k
+
+
+def mx8_scale_exp(amax: float) -> int:
+    """Exponent e of the MXFP8 block scale for a block maximum amax >= 0."""
+    bits = int(np.array([amax], dtype=np.float32).view(np.uint32)[0])
+    return lib().oracle_mx8_scale_exp(bits)
+
+
+def mxfp8_quantize(x, axis: int = 1) -> MX8Quantized:
+    a, dt = _as_raw(x)
+    a = np.ascontiguousarray(a)
+    rows, cols = a.shape
+    outer, K = (rows, cols) if axis else (cols, rows)
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    codes = np.zeros((outer, K), dtype=np.uint8)
+    scales = np.zeros((outer, K // 32), dtype=np.uint8)
+    rc = lib().oracle_mxfp8_quantize(_ptr(a), dt, rows, cols, axis, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp8_quantize failed: {rc}")
+    return MX8Quantized(codes, scales, outer, K)
+
+
+def mxfp8_decode(q: MX8Quantized, rows=None) -> np.ndarray:
+    """Exact values e4m3(code) * 2^e of the selected outer rows, float64 [n][K]."""
+    if rows is None:
+        rows = np.arange(q.outer, dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.zeros((rows.size, q.k), dtype=np.float64)
+    rc = lib().oracle_mxfp8_decode(_ptr(q.codes), _ptr(q.scales), q.k, _ptr(rows), rows.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp8_decode failed: {rc}")
+    return out
+
+
+def mxfp8_gemm(qa: MX8Quantized, qb: MX8Quantized, rows=None, cols=None):
+    """GEMM oracle C = A B^T of the decoded MXFP8 operands, float64 (every
+    product is exact in float64).  Returns (C, bound) as gemm() does."""
+    if qa.k != qb.k:
+        raise ValueError("K mismatch")
+    da = mxfp8_decode(qa, rows)
+    db = mxfp8_decode(qb, cols)
+    return da @ db.T, np.abs(da) @ np.abs(db).T
+
+
+def mxfp8_trunc_bound(qa: MX8Quantized, qb: MX8Quantized, rows=None, cols=None) -> np.ndarray:
+    """Per-element bound of what the FP8 block-scaled MFMA loses to its product
+    truncation (the C function states the measured reading); the MXFP8 GEMM
+    tolerance is this plus rtol * sum|ab|."""
+    if qa.k != qb.k:
+        raise ValueError("K mismatch")
+    ra = np.ascontiguousarray(np.arange(qa.outer) if rows is None else np.asarray(rows), dtype=np.int64)
+    rb = np.ascontiguousarray(np.arange(qb.outer) if cols is None else np.asarray(cols), dtype=np.int64)
+    out = np.zeros((ra.size, rb.size), dtype=np.float64)
+    rc = lib().oracle_mxfp8_trunc_bound(_ptr(qa.codes), _ptr(qa.scales), _ptr(qb.codes), _ptr(qb.scales), qa.k,
+                                        _ptr(ra), ra.size, _ptr(rb), rb.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp8_trunc_bound failed: {rc}")
+    return out
+
+
+def check_gemm_mx8_f32(c_gpu: np.ndarray, c_ref: np.ndarray, bound: np.ndarray, trunc: np.ndarray,
+                       rtol: float = 1e-5):
+    """MXFP8 tolerance rule for f32 output: |C - Cref| <= trunc + rtol * bound
+    elementwise.  Returns (ok, worst |err| / (trunc + rtol * bound), worst
+    |err| / bound)."""
+    c = np.asarray(c_gpu, dtype=np.float64)
+    err = np.abs(c - c_ref)
+    lim = trunc + rtol * bound
+    ok = bool(np.all(err <= lim))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r1 = np.where(lim > 0, err / np.where(lim > 0, lim, 1.0), np.where(err > 0, np.inf, 0.0))
+        r2 = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    return ok, float(np.max(r1)) if r1.size else 0.0, float(np.max(r2)) if r2.size else 0.0

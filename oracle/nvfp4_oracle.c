@@ -31,6 +31,9 @@
  *   oracle_philox4x32_10                                    pinned (rocRAND)
  *   oracle_rht16                                            pinned
  *   oracle_quantize / oracle_dequantize / oracle_decode_qs  pinned
+ *   oracle_mx_scale_exp / oracle_mxfp4_quantize / _decode   pinned
+ *   oracle_mx8_scale_exp / oracle_mxfp8_quantize / _decode  pinned
+ *   oracle_mxfp8_trunc_bound (a tolerance checker)          worked cases
  */
 #include <math.h>
 #include <stdint.h>
@@ -505,6 +508,137 @@ int oracle_mxfp4_decode(const uint8_t *codes, const uint8_t *scales, int64_t K,
             uint8_t q = (k & 1) ? (byte >> 4) : (byte & 15);
             int e = (int)scales[o * (K / 32) + k / 32] - 127;
             out[r * K + k] = ldexp((double)oracle_e2m1_value(q), e);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------- MXFP8 ----
+ * The 8-bit member of the microscaling family: one of the three number
+ * formats of the training run in [P3] "Drei Formate, ein Trainingslauf"
+ * (about 5 PFLOPS on GB300), and the block layout NVFP4 is contrasted with
+ * in [P4] "Architektura NVFP4 kontra ograniczenia mikroskalowania" (blocks of
+ * 32 elements sharing a power-of-two scale).  Elements are OCP E4M3FN (bias
+ * 7, largest 448, subnormals down to 2^-9), one byte each; each 32-block
+ * along K carries one E8M0 exponent (scale 2^(code - 127)); no tensor scale.
+ * Readings, as for MXFP4: the block scale is the smallest power of two
+ * X = 2^e with amax_b / X <= 448, so the block maximum is never clipped, e
+ * clamped to [-127, 127], an all-zero block takes e = -127; each element is
+ * the nearest-even E4M3 code of x / X with the sign of x kept (-0.0 and
+ * negatives that round to zero give 0x80). */
+
+/* Smallest e with amax <= 448 * 2^e, from the bit pattern of amax >= 0.
+ * 448 * 2^e = 1.75 * 2^(e+8): for amax = m * 2^E (m in [1,2)) that is
+ * e = E - 8 when m <= 1.75, else e = E - 7.  Zero and subnormal maxima fit
+ * e = -127. */
+int oracle_mx8_scale_exp(uint32_t amax_bits)
+{
+    amax_bits &= 0x7FFFFFFFu;
+    if (amax_bits < 0x00800000u) return -127;
+    int E = (int)(amax_bits >> 23) - 127;
+    uint32_t mant = amax_bits & 0x7FFFFFu;
+    int e = (mant <= 0x600000u) ? E - 8 : E - 7;        /* m <= 1.75 ? */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+int oracle_mxfp8_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
+                          int axis, uint8_t *codes, uint8_t *scales)
+{
+    if (rows < 0 || cols < 0) return -2;
+    int64_t outer = axis ? rows : cols;
+    int64_t K = axis ? cols : rows;
+    if (K % 32 != 0) return -2;
+    int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < outer; ++o) {
+        for (int64_t b = 0; b < nb; ++b) {
+            float y[32];
+            uint32_t bmax = 0;
+            for (int j = 0; j < 32; ++j) {
+                y[j] = view_get(x, dtype, rows, cols, axis, o, 32 * b + j);
+                uint32_t a = f32_bits(y[j]) & 0x7FFFFFFFu;
+                if (a > bmax) bmax = a;
+            }
+            int e = oracle_mx8_scale_exp(bmax);
+            scales[o * nb + b] = (uint8_t)(e + 127);
+            for (int j = 0; j < 32; ++j) {
+                /* x / 2^e is exact in double; its magnitude is <= 448, so the
+                 * binary32 cast is exact down to 2^-149, far below half the
+                 * smallest E4M3 step (2^-10) */
+                float v = (float)ldexp((double)y[j], -e);
+                uint8_t sign = signbit(v) ? 0x80 : 0x00;
+                codes[o * K + 32 * b + j] = (uint8_t)(sign | oracle_e4m3_rne_sat(fabsf(v)));
+            }
+        }
+    }
+    return 0;
+}
+
+/* Exact value e4m3(code) * 2^(scale - 127) of the selected outer rows. */
+int oracle_mxfp8_decode(const uint8_t *codes, const uint8_t *scales, int64_t K,
+                        const int64_t *rows_sel, int64_t n_sel, double *out)
+{
+    if (K < 0 || K % 32 != 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_sel; ++r) {
+        int64_t o = rows_sel[r];
+        for (int64_t k = 0; k < K; ++k) {
+            int e = (int)scales[o * (K / 32) + k / 32] - 127;
+            out[r * K + k] = ldexp((double)oracle_e4m3_value(codes[o * K + k]), e);
+        }
+    }
+    return 0;
+}
+
+/* Checker (part of the tolerance, not of the method): the most the FP8
+ * block-scaled MFMA can lose to its product truncation, per output element.
+ * Reading of the instruction, from device measurements on MI355X: the 64
+ * products of one instruction are summed in groups of 8 consecutive K
+ * positions (aligned runs of 8); within a group every product is truncated
+ * toward zero to a multiple of 2^(E - 13), where E is the largest
+ * exponent(a) + exponent(b) over the group plus the two block-scale
+ * exponents (exponent(x) = floor(log2|x|) for a normal E4M3 value, -6 for a
+ * subnormal or zero); group results and the accumulator are then added and
+ * rounded to binary32 once.  A product with exponent(a) + exponent(b) >= E - 7
+ * has no bits below 2^(E - 13) and is exact; any other loses less than
+ * min(|p|, 2^(E - 13)).  out[i][j] = the sum of those losses over all groups
+ * of row rows_a[i] of A and row rows_b[j] of B (K % 32 == 0). */
+static int e4m3_exponent(uint8_t c)
+{
+    int f = (c >> 3) & 15;
+    return f == 0 ? -6 : f - 7;
+}
+
+int oracle_mxfp8_trunc_bound(const uint8_t *codes_a, const uint8_t *scales_a,
+                             const uint8_t *codes_b, const uint8_t *scales_b, int64_t K,
+                             const int64_t *rows_a, int64_t na,
+                             const int64_t *rows_b, int64_t nb, double *out)
+{
+    if (K < 0 || K % 32 != 0) return -2;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < na; ++i) {
+        for (int64_t j = 0; j < nb; ++j) {
+            const uint8_t *a = codes_a + rows_a[i] * K, *b = codes_b + rows_b[j] * K;
+            const uint8_t *sa = scales_a + rows_a[i] * (K / 32), *sb = scales_b + rows_b[j] * (K / 32);
+            double t = 0.0;
+            for (int64_t g = 0; g < K / 8; ++g) {
+                int s = ((int)sa[g / 4] - 127) + ((int)sb[g / 4] - 127);
+                int ex[8], E = -1000;
+                for (int q = 0; q < 8; ++q) {
+                    ex[q] = e4m3_exponent(a[8 * g + q]) + e4m3_exponent(b[8 * g + q]);
+                    if (ex[q] > E) E = ex[q];
+                }
+                double unit = ldexp(1.0, E + s - 13);
+                for (int q = 0; q < 8; ++q) {
+                    if (ex[q] >= E - 7) continue;
+                    double p = fabs((double)oracle_e4m3_value(a[8 * g + q]) *
+                                    (double)oracle_e4m3_value(b[8 * g + q])) * ldexp(1.0, s);
+                    t += p < unit ? p : unit;
+                }
+            }
+            out[i * nb + j] = t;
         }
     }
     return 0;
