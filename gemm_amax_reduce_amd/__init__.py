@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = ["NVFP4Tensor", "NVFP4Error", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_amax",
-           "nvfp4_quantize_amax", "MXFP4Tensor", "mxfp4_quantize", "mxfp4_gemm",
+           "nvfp4_quantize_amax", "MXFP4Tensor", "mxfp4_quantize", "mxfp4_gemm", "MXFP8Tensor", "mxfp8_quantize",
+           "mxfp8_gemm",
            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws", "nvfp4_gemm_noalloc", "gemm_workspace", "lib", "LIB_PATH", "F32", "BF16", "RNE", "SR"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +46,8 @@ _lib = None
 # every symbol the header declares
 EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_quantize_dual",
            "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws",
-           "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_noalloc", "nvfp4_probe_mfma", "nvfp4_status_string")
+           "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_noalloc", "mxfp8_quantize", "mxfp8_gemm", "nvfp4_probe_mfma",
+           "nvfp4_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -67,6 +69,10 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_quantize.restype = ci
         L.mxfp4_gemm.argtypes = [mt, mt, vp, ci, i64, vp]
         L.mxfp4_gemm.restype = ci
+        L.mxfp8_quantize.argtypes = [vp, ci, i64, i64, ci, mt, vp]
+        L.mxfp8_quantize.restype = ci
+        L.mxfp8_gemm.argtypes = [mt, mt, vp, ci, i64, vp]
+        L.mxfp8_gemm.restype = ci
         L.nvfp4_amax.argtypes = [vp, ci, i64, i64, ci, ci, ctypes.c_uint16, vp, vp]
         L.nvfp4_amax.restype = ci
         L.nvfp4_quantize_amax.argtypes = [vp, ci, i64, i64, ci, ci, u64, u64, ci, ctypes.c_uint16, vp, pt, vp]
@@ -455,3 +461,64 @@ def mxfp4_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out_dtype=torch.float32, out: tor
                                 _stream_handle(stream, dev)), "mxfp4_gemm")
     return out
 
+
+
+class MXFP8Tensor:
+    """Device buffers of one MXFP8 tensor in its quantized [outer][k] layout:
+    ``codes`` u8 [outer, k] (E4M3), ``scales`` u8 [outer, k/32] (E8M0).  The
+    C struct has the same fields as the MXFP4 one."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, outer: int, k: int):
+        self.codes, self.scales, self.outer, self.k = codes, scales, int(outer), int(k)
+
+    @classmethod
+    def empty(cls, outer: int, k: int, device=None) -> "MXFP8Tensor":
+        device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        return cls(torch.empty((outer, k), dtype=torch.uint8, device=device),
+                   torch.empty((outer, k // 32), dtype=torch.uint8, device=device), outer, k)
+
+    @property
+    def device(self) -> torch.device:
+        return self.codes.device
+
+    def _c(self) -> _MXTensor:
+        if self.outer < 0 or self.k < 0 or self.k % 32:
+            raise NVFP4Error(f"invalid MXFP8 shape ({self.outer}, {self.k})")
+        dev = self.codes.device
+        _require_buffer(self.codes, "codes", torch.uint8, self.outer * self.k, dev)
+        _require_buffer(self.scales, "scales", torch.uint8, self.outer * (self.k // 32), dev)
+        return _MXTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.outer, self.k)
+
+
+def mxfp8_quantize(x: torch.Tensor, axis: int = 1, out: MXFP8Tensor | None = None, stream=None) -> MXFP8Tensor:
+    """Quantize a 2-D f32/bf16 GPU tensor to MXFP8 (see include/nvfp4.h)."""
+    _require_device(x, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise NVFP4Error("x must be a contiguous 2-D tensor")
+    rows, cols = x.shape
+    outer, k = (rows, cols) if axis == 1 else (cols, rows)
+    if out is None:
+        out = MXFP8Tensor.empty(outer, k, device=x.device)
+    _same_device(out, x)
+    ct = out._c()
+    with torch.cuda.device(x.device):
+        _check(lib().mxfp8_quantize(x.data_ptr(), _dtype_code(x), rows, cols, axis, ctypes.byref(ct),
+                                    _stream_handle(stream, x.device)), "mxfp8_quantize")
+    return out
+
+
+def mxfp8_gemm(a: MXFP8Tensor, b: MXFP8Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """C = A . B^T for MXFP8 A [M, K] and B [N, K] (K % 128 == 0), f32 accumulation."""
+    code = _out_code(out_dtype)
+    dev = a.device
+    if b.device != dev:
+        raise NVFP4Error(f"operands on {a.device} and {b.device}")
+    if out is None:
+        out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=dev)
+    ldc = _require_matrix_out(out, a.outer, b.outer, out_dtype, dev)
+    ca, cb = a._c(), b._c()
+    with torch.cuda.device(dev):
+        _check(lib().mxfp8_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), code, ldc,
+                                _stream_handle(stream, dev)), "mxfp8_gemm")
+    return out

@@ -14,6 +14,10 @@ namespace {
 // for MXFP4.
 constexpr int64_t kMaxRowsAxis0 = 65535LL * 4 * 16;       // 4 194 240
 constexpr int64_t kMaxRowsAxis0Mx = 65535LL * 8 * 32;     // 16 776 960
+constexpr int64_t kMaxRowsAxis0Mx8 = 65535LL * 4 * 32;    // 8 388 480
+// The MXFP8 GEMM addresses 128 operand rows of K code bytes with 32-bit
+// buffer offsets below 2^31.
+constexpr int64_t kMaxGemmKMx8 = (1LL << 24) - 128;
 // The GEMMs address 128 operand rows of K/2 code bytes with 32-bit buffer
 // offsets below 2^31, and launch at most INT32_MAX workgroups (tiles of
 // 256 x 128 or larger).
@@ -190,6 +194,38 @@ int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int c_dtyp
     return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_mx_gemm(a->codes, a->scales, b->codes, b->scales, M, N, a->k, c, c_dtype, ldc,
                                           (hipStream_t)hip_stream));
+}
+
+int mxfp8_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, mxfp8_tensor *out,
+                   void *hip_stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  if (axis != 0 && axis != 1) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0 || !count_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+  const int64_t outer = axis ? rows : cols, k = axis ? cols : rows;
+  if (k % 32 != 0 || out->outer != outer || out->k != k) return NVFP4_ERR_SHAPE;
+  if (axis == 0 && rows > kMaxRowsAxis0Mx8) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (!x || !out->codes || !out->scales)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out->codes, 16)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_mx8_quantize(x, x_dtype, rows, cols, axis, out->codes, out->scales,
+                                               (hipStream_t)hip_stream));
+}
+
+int mxfp8_gemm(const mxfp8_tensor *a, const mxfp8_tensor *b, void *c, int c_dtype, int64_t ldc, void *hip_stream) {
+  if (!a || !b) return NVFP4_ERR_NULL;
+  if (a->outer < 0 || b->outer < 0 || a->k < 0 || a->k != b->k || a->k % 128 != 0) return NVFP4_ERR_SHAPE;
+  if (a->k > kMaxGemmKMx8 || !count_ok(a->outer, a->k) || !count_ok(b->outer, b->k)) return NVFP4_ERR_SHAPE;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ENUM;
+  const int64_t M = a->outer, N = b->outer;
+  if (ldc < N || !count_ok(M, ldc) || !gemm_shape_ok(M, N, 0)) return NVFP4_ERR_SHAPE;
+  if (M > 0 && N > 0 && (!c || (a->k > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
+    return NVFP4_ERR_NULL;
+  if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_ALIGN;
+  // the kernel moves codes in 16-byte and scales in 4-byte pieces by DMA
+  if (!aligned(a->codes, 16) || !aligned(b->codes, 16) || !aligned(a->scales, 4) || !aligned(b->scales, 4))
+    return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_mx8_gemm(a->codes, a->scales, b->codes, b->scales, M, N, a->k, c, c_dtype, ldc,
+                                           (hipStream_t)hip_stream));
 }
 
 int nvfp4_dequantize(const nvfp4_tensor *q, void *y, int y_dtype, void *hip_stream) {

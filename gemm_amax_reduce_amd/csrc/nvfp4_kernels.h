@@ -43,6 +43,14 @@ hipError_t launch_mx_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const
                           const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
                           hipStream_t stream);
 
+// MXFP8 (32-element E4M3 blocks with E8M0 scales): quantize on axis 1 or 0,
+// and C = A . B^T on the block-scaled FP8 MFMA (K % 128 == 0).
+hipError_t launch_mx8_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, uint8_t *codes,
+                               uint8_t *scales, hipStream_t stream);
+hipError_t launch_mx8_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                           const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
+                           hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *meta, int64_t outer,
                              int64_t k, void *y, int y_dtype, hipStream_t stream);
 

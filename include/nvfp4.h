@@ -29,7 +29,8 @@
  *  - Sizes are int64_t and may be 0 (empty tensors are valid, see below).
  *    Limits of the launch geometry (NVFP4_ERR_SHAPE beyond them):
  *    quantization down the columns (axis 0, and the dual call) takes
- *    rows <= 4 194 240 (MXFP4: 16 776 960); the GEMMs take K <= 2^25 - 16
+ *    rows <= 4 194 240 (MXFP4: 16 776 960, MXFP8: 8 388 480); the NVFP4
+ *    GEMMs take K <= 2^25 - 16 (MXFP8: K <= 2^24 - 128)
  *    and ceil(M/256) * ceil(N/128) <= INT32_MAX; every element count
  *    (rows * cols, outer * k, M * ldc) is at most 2^60.
  *  - Element types: NVFP4_F32 (binary32) or NVFP4_BF16 (bfloat16).
@@ -309,6 +310,53 @@ int mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int a
  * even).  Accuracy as nvfp4_gemm: within 1e-5 * sum_k |a b|.  Deterministic.
  */
 int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int c_dtype,
+               int64_t ldc, void *hip_stream);
+
+/*
+ * MXFP8 -- the 8-bit microscaling format, one of the three number formats
+ * of a training run in [P3] "Drei Formate, ein Trainingslauf" (the one
+ * quoted at about 5 PFLOPS on GB300), with the 32-element power-of-two
+ * blocks of [P4] "Architektura NVFP4 kontra ograniczenia mikroskalowania".
+ *  codes  : u8 [outer][k], OCP E4M3FN bytes (bias 7, max 448), 16-byte
+ *           aligned.
+ *  scales : u8 [outer][k/32], E8M0 exponents: the block scale is
+ *           2^(code - 127).  4-byte aligned for a GEMM operand.
+ *  outer, k : k % 32 == 0.
+ * The value of element (o, kk) is e4m3(code) * 2^(scale - 127).
+ */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    int64_t outer;
+    int64_t k;
+} mxfp8_tensor;
+
+/*
+ * mxfp8_quantize -- x (row-major [rows][cols], x_dtype, 16-byte aligned)
+ * viewed on `axis` as in nvfp4_quantize.  Per 32-block along k: the scale is
+ * the smallest power of two 2^e with blockmax / 2^e <= 448 (e clamped to
+ * [-127, 127]; an all-zero block takes e = -127), so the block maximum is
+ * never clipped; each element is the nearest-even E4M3 code of x / 2^e with
+ * the sign of x (-0.0 gives 0x80).  Axis 0 takes rows <= 8 388 480.
+ * Enqueues one kernel.
+ */
+int mxfp8_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis,
+                   mxfp8_tensor *out, void *hip_stream);
+
+/*
+ * mxfp8_gemm -- C[m][n] = sum_k (qA * 2^eA)[m][k] * (qB * 2^eB)[n][k] with
+ * FP32 accumulation on gfx950's block-scaled FP8 MFMA (the codes are not
+ * decoded).  a: M x K, b: N x K, both K-contiguous; K % 128 == 0 and
+ * K <= 2^24 - 128 (NVFP4_ERR_SHAPE otherwise).  c: row-major [M][ldc], f32
+ * or bf16 (nearest even).  Accuracy: the instruction sums its 64 products
+ * per step in groups of 8 consecutive K positions and truncates each
+ * product toward zero to 13 bits below the group's largest exponent sum
+ * (measured on MI355X), so an element can lose up to
+ * sum over groups of sum_k min(|a_k b_k|, 2^(E_group - 13)) on top of the
+ * binary32 accumulation of about K/64 steps; every element lies within
+ * that bound plus 1e-5 * sum_k |a b| of the exact value.  Deterministic.
+ */
+int mxfp8_gemm(const mxfp8_tensor *a, const mxfp8_tensor *b, void *c, int c_dtype,
                int64_t ldc, void *hip_stream);
 
 /*

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:nvfp4|mxfp4)_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:nvfp4|mxfp4|mxfp8)_[a-z_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
