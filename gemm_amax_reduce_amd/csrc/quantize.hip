@@ -342,6 +342,41 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
       sc[e] |= S << (8 * i);
     }
   }
+  // A full workgroup tile (its 64 * CPT columns x 16 blocks all inside
+  // the tensor) is 64 * CPT whole 128-byte code lines and as many 16-byte
+  // scale runs: staged through LDS, so each store instruction writes 8
+  // whole lines (the lanes' own 32-byte pieces went to 64 lines per
+  // instruction).  Tiles at the edges store their pieces directly.
+  constexpr int kCols = 64 * CPT;
+  __shared__ __attribute__((aligned(16))) uint2 tile_codes[kCols][4 * kNBT + 2];   // 144-byte rows: no bank conflicts
+  __shared__ __attribute__((aligned(16))) uint32_t tile_scales[kCols][kNBT];
+  const int64_t c_wg = (int64_t)(gridDim.x - 1 - blockIdx.x) * kCols;
+  const int64_t kb_wg = (int64_t)(gridDim.y - 1 - blockIdx.y) * 4 * kNBT;
+  const bool whole = (c_wg + kCols <= cols) && (kb_wg + 4 * kNBT <= nkb) && (nkb % 2 == 0) &&
+                     aligned_to(codes, 16) && aligned_to(scales, 16) && (nkb % 16 == 0);
+  if (whole) {
+    const int cl = lane * CPT;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+#pragma unroll
+      for (int i = 0; i < kNBT; ++i) tile_codes[cl + e][wave * kNBT + i] = cw[e][i];
+      tile_scales[cl + e][wave] = sc[e];
+    }
+    __syncthreads();
+    // codes: column q / 8, 16-byte piece q % 8 of its 128-byte line
+#pragma unroll
+    for (int r = 0; r < kCols * 8 / kQT; ++r) {
+      const int q = r * kQT + (int)threadIdx.x, col = q >> 3, piece = q & 7;
+      const uint4 v = *reinterpret_cast<const uint4 *>(&tile_codes[col][2 * piece]);
+      *reinterpret_cast<uint4 *>(codes + (c_wg + col) * nkb + kb_wg + 2 * piece) = v;
+    }
+    // scales: one 16-byte run per column
+    if (threadIdx.x < kCols) {
+      const int col = threadIdx.x;
+      *reinterpret_cast<uint4 *>(scales + (c_wg + col) * nkb + kb_wg) = *reinterpret_cast<const uint4 *>(tile_scales[col]);
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < CPT; ++e) {
     if (c + e >= cols) break;
