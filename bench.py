@@ -233,7 +233,8 @@ def reduce_busy(busy_dir: str) -> str:
     """MFMA busy fraction, clock and issue counters of the GEMM kernels from
     one rocprofv3 --pmc run of this script; returns the markdown summary."""
     ds = _dispatches(busy_dir)
-    kinds = (("k_gemm_nvfp4<true, true>", "fprop"), ("k_gemm_nvfp4<false, true>", "dgrad + wgrad"))
+    kinds = (("k_gemm_nvfp4<true, true>", "fprop"), ("k_gemm_nvfp4_split<false, true>", "dgrad"),
+             ("k_gemm_nvfp4<false, true>", "wgrad"))
     lines = ["# MFMA busy fraction and clock of the GEMM kernels (linear-layer step)", "",
              "Command (repository root, one MI355X; one counter pass, 7 SQ + 1 GRBM counters), then the reduction:",
              "", "```",
@@ -364,22 +365,26 @@ def main():
     qX2 = nv.NVFP4Tensor.empty(5120, 8192)
     qdYt = nv.NVFP4Tensor.empty(20480, 8192)
     Y = torch.empty((4096, 5120), dtype=torch.bfloat16, device=dev)
+    # the GEMMs run through nvfp4_gemm_ws: it cuts the tiles of a partly
+    # filled last round into K ranges where that is faster (dgrad) and runs
+    # the mixed-width grid of nvfp4_gemm otherwise (fprop, wgrad)
+    ws = nv.gemm_workspace(dev)
     dX = torch.empty((8192, 5120), dtype=torch.float32, device=dev)
     dW = torch.empty((5120, 20480), dtype=torch.float32, device=dev)
 
     ops = [
         ("q fprop X", lambda: nv.nvfp4_quantize(X1, axis=1, out=qX1), ("q", X1)),
         ("q fprop W", lambda: nv.nvfp4_quantize(W1, axis=1, out=qW1), ("q", W1)),
-        ("gemm fprop", lambda: nv.nvfp4_gemm(qX1, qW1, torch.bfloat16, out=Y), ("g", F.flops)),
+        ("gemm fprop", lambda: nv.nvfp4_gemm_ws(qX1, qW1, torch.bfloat16, out=Y, workspace=ws), ("g", F.flops)),
         # dY in both layouts from one amax read: axis 1 SR (dgrad, offset 0)
         # and axis 0 RHT SR (wgrad, offset 1)
         ("q dY dual (axis1 SR + axis0 RHT SR)",
          lambda: nv.nvfp4_quantize_dual(dY, rounding1="sr", seed1=seed, offset1=0, rht0=True, sign_mask0=mask,
                                         rounding0="sr", seed0=seed, offset0=1, out1=qdY, out0=qdYt), ("q2", dY)),
         ("q dgrad W (axis0)", lambda: nv.nvfp4_quantize(W2, axis=0, out=qW2), ("q", W2)),
-        ("gemm dgrad", lambda: nv.nvfp4_gemm(qdY, qW2, torch.float32, out=dX), ("g", D.flops)),
+        ("gemm dgrad", lambda: nv.nvfp4_gemm_ws(qdY, qW2, torch.float32, out=dX, workspace=ws), ("g", D.flops)),
         ("q wgrad X (RHT, axis0)", lambda: nv.nvfp4_rht_quantize(X2, mask, axis=0, out=qX2), ("q", X2)),
-        ("gemm wgrad", lambda: nv.nvfp4_gemm(qX2, qdYt, torch.float32, out=dW), ("g", Wg.flops)),
+        ("gemm wgrad", lambda: nv.nvfp4_gemm_ws(qX2, qdYt, torch.float32, out=dW, workspace=ws), ("g", Wg.flops)),
     ]
     step_flops = F.flops + D.flops + Wg.flops
     # The backward operands that come from forward-time tensors (W on axis 0
@@ -462,28 +467,35 @@ def main():
         if release_after < i < first_wait:
             breakdown[ops[i][0]]["stream"] = "main, overlapped with the second stream's quantizations"
 
-    # dominant kernel: the f32-output GEMM kernel (dgrad and wgrad launches,
-    # each 2*8192*5120*20480 flop); one nvfp4_gemm call is one kernel launch
-    # on torch's current stream, which the events above are recorded on
-    gi = [i for i, (n, _, _) in enumerate(ops) if n in ("gemm dgrad", "gemm wgrad")]
+    # dominant kernel: the one kernel with the most time per step, the
+    # f32-output data-parallel GEMM of wgrad (2*5120*20480*8192 flop per
+    # launch; dgrad's launch is the split kernel, fprop's the bf16 one); one
+    # GEMM call is one kernel launch on torch's current stream, which the
+    # events above are recorded on
+    gi = [i for i, (n, _, _) in enumerate(ops) if n == "gemm wgrad"]
     g_ms = float(np.mean(per_op[:, gi]))
-    g_flop = D.flops
+    g_flop = Wg.flops
     achieved = g_flop / (g_ms * 1e-3) / 1e12
     traffic = load_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                 "traffic": round(traffic) if traffic else None,
-                "kernel": DOMINANT + " (f32 out), avg of the dgrad and wgrad launches",
+                "kernel": DOMINANT + " (f32 out, data-parallel grid): the wgrad launch of each step",
                 "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flop,
-                "algorithmic_bytes_per_launch": int(np.mean([gemm_bytes(D), gemm_bytes(Wg)])),
+                "algorithmic_bytes_per_launch": gemm_bytes(Wg),
                 "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4),
-                "frac_of_measured_mfma_probe": round(achieved / measured_peaks["mfma_f16_probe_TFLOP/s"], 4)}
+                "frac_of_measured_mfma_probe": round(achieved / measured_peaks["mfma_f16_probe_TFLOP/s"], 4),
+                "gemm_kernels": {"fprop": "k_gemm_nvfp4<true, true> (bf16 out, mixed 256/128-wide grid)",
+                                 "dgrad": "k_gemm_nvfp4_split<false, true> (f32 out, tail split in two K ranges)",
+                                 "wgrad": DOMINANT + " (f32 out, mixed 256/128-wide grid)"}}
 
     # ------------------------------------------------ quantizer sweep ----
     sweep = None
     dequant = None
+    T_host = None
     if not args.no_sweep:
-        T = workloads.SWEEP.generate().to(dev)
+        T_host = workloads.SWEEP.generate()
+        T = T_host.to(dev)
         qT = nv.NVFP4Tensor.empty(32768, 8192)
         qTt = nv.NVFP4Tensor.empty(8192, 32768)
         b = qbytes(T.numel(), 2)
@@ -510,7 +522,35 @@ def main():
                     ms = e0.elapsed_time(e1) / n_it
                     gbs = b / (ms * 1e-3) / 1e9
                     sweep[f"axis{axis} {rnd}{'+rht' if rht else ''}"] = {
-                        "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4)}
+                        "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4),
+                        "frac_of_measured_copy": round(gbs / measured_peaks["hbm_copy_GB/s"], 4)}
+        # each pass alone (the encode pass with the amax supplied, so it reads
+        # the tensor cold, without the MALL reuse the whole call has), and the
+        # stochastic-rounding random bits alone (Philox4x32-10 for the
+        # tensor's n/8 counters, no memory traffic): the floor the RNG
+        # contract puts under an SR encode of this tensor
+        amax_buf = torch.empty(1, dtype=torch.float32, device=dev)
+        def _t(fn, it=10):
+            for _ in range(2):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(it):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / it
+        passes = {"philox_floor_ms": round(sorted(nv.nvfp4_probe_philox(T.numel() // 8) for _ in range(5))[2], 4)}
+        for axis in (1, 0):
+            out = qT if axis == 1 else qTt
+            for rnd in ("rne", "sr"):
+                for rht in (False, True):
+                    a_ms = _t(lambda: nv.nvfp4_amax(T, axis=axis, rht=rht, sign_mask=mask, out=amax_buf))
+                    e_ms = _t(lambda: nv.nvfp4_quantize_amax(T, amax_buf, axis=axis, rounding=rnd, seed=seed,
+                                                             rht=rht, sign_mask=mask, out=out))
+                    passes[f"axis{axis} {rnd}{'+rht' if rht else ''}"] = {"amax_pass_ms": round(a_ms, 4),
+                                                                          "encode_pass_ms": round(e_ms, 4)}
+        sweep["passes"] = passes
         # dequantize of the same tensor (the last axis-1 result): codes and
         # scales read once (0.5625 B/element), values written once
         dequant = {}
@@ -639,10 +679,60 @@ def main():
             mx_ctx["breakdown"][name] = ent
         del mX1, mW1, mdY, mW2, mX2, mdYt
 
+    # ------------------------------------------------ MXFP8 context ----
+    # The same step in MXFP8 (E4M3 elements, a power-of-two scale per 32) on
+    # the block-scaled FP8 MFMA: the 8-bit format of the pages' three-format
+    # training run.  Context only.
+    mx8_ctx = None
+    if not args.no_sweep:
+        PEAK_FP8_TFLOPS = 5000.0
+        eX1 = nv.MXFP8Tensor.empty(4096, 5120)
+        eW1 = nv.MXFP8Tensor.empty(5120, 5120)
+        edY = nv.MXFP8Tensor.empty(8192, 20480)
+        eW2 = nv.MXFP8Tensor.empty(5120, 20480)
+        eX2 = nv.MXFP8Tensor.empty(5120, 8192)
+        edYt = nv.MXFP8Tensor.empty(20480, 8192)
+        mx8_ops = [
+            ("q fprop X", lambda: nv.mxfp8_quantize(X1, axis=1, out=eX1)),
+            ("q fprop W", lambda: nv.mxfp8_quantize(W1, axis=1, out=eW1)),
+            ("gemm fprop", lambda: nv.mxfp8_gemm(eX1, eW1, torch.bfloat16, out=Y)),
+            ("q dgrad dY", lambda: nv.mxfp8_quantize(dY, axis=1, out=edY)),
+            ("q dgrad W (axis0)", lambda: nv.mxfp8_quantize(W2, axis=0, out=eW2)),
+            ("gemm dgrad", lambda: nv.mxfp8_gemm(edY, eW2, torch.float32, out=dX)),
+            ("q wgrad X (axis0)", lambda: nv.mxfp8_quantize(X2, axis=0, out=eX2)),
+            ("q wgrad dY (axis0)", lambda: nv.mxfp8_quantize(dY, axis=0, out=edYt)),
+            ("gemm wgrad", lambda: nv.mxfp8_gemm(eX2, edYt, torch.float32, out=dW)),
+        ]
+        for _ in range(2):
+            for _, fn in mx8_ops:
+                fn()
+        n_mx = 10
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(mx8_ops) + 1)] for _ in range(n_mx)]
+        torch.cuda.synchronize()
+        for it in range(n_mx):
+            ev[it][0].record()
+            for i, (_, fn) in enumerate(mx8_ops):
+                fn()
+                ev[it][i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([[ev[it][i].elapsed_time(ev[it][i + 1]) for i in range(len(mx8_ops))] for it in range(n_mx)])
+        step_mx8 = float(np.median(per.sum(axis=1)))
+        mx8_ctx = {"ms_per_step": round(step_mx8, 4), "TFLOP/s": round(step_flops / (step_mx8 * 1e-3) / 1e12, 1),
+                   "breakdown": {}}
+        flops_of = {"gemm fprop": F.flops, "gemm dgrad": D.flops, "gemm wgrad": Wg.flops}
+        for i, (name, _) in enumerate(mx8_ops):
+            ms = float(np.median(per[:, i]))
+            ent = {"ms": round(ms, 4)}
+            if name in flops_of:
+                ent["TFLOP/s"] = round(flops_of[name] / (ms * 1e-3) / 1e12, 1)
+                ent["frac_of_fp8_peak"] = round(flops_of[name] / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
+            mx8_ctx["breakdown"][name] = ent
+        del eX1, eW1, edY, eW2, eX2, edYt
+
     # ------------------------------------------------- CPU baseline ----
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(F, D, Wg, mask, seed, step_flops)
+        cpu = cpu_baseline(F, D, Wg, mask, seed, step_flops, T_host)
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
@@ -661,6 +751,7 @@ def main():
         "fprop_quantize_warm_vs_flushed": fprop_cache,
         "bf16_gemm_context": bf16_ctx,
         "mxfp4_step_context": mx_ctx,
+        "mxfp8_step_context": mx8_ctx,
         "pages_context": PAGES_CONTEXT,
         "device": torch.cuda.get_device_name(0),
         "step_ms_event_median": round(float(np.median(step_ms)), 4),
@@ -680,20 +771,52 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(F, D, Wg, mask, seed, step_flops):
-    """The oracle (plain C + numpy float64) on a bounded sample of the step:
-    all six quantizations in full, and for each GEMM the full oracle on a
-    slice of 512 output rows; the step time is extrapolated as
-    t(quantize) + sum_g t(slice_g) * M_g / 512."""
+def blas_threads():
+    """Threads of the BLAS numpy's float64 matmul runs on (the GEMM oracle)."""
+    try:
+        import threadpoolctl
+        info = [d for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        return int(info[0]["num_threads"]) if info else None
+    except Exception:
+        return None
+
+
+def cpu_baseline(F, D, Wg, mask, seed, step_flops, sweep_host=None):
+    """The oracle (plain C with OpenMP + numpy float64) on the host cores:
+
+    * quantizer: all eight variants ({RNE, SR} x {no RHT, RHT} x {axis 1,
+      axis 0}) on the full 32768 x 8192 sweep tensor, as GB/s with the same
+      4.5625 B/element formula as the GPU;
+    * GEMM: the full fprop oracle (4096 x 5120 x 5120, value and bound);
+      dgrad and wgrad on 512-row slices, extrapolated to the full M
+      (labelled so);
+    * the step: its six quantizations in full plus the three GEMMs, as
+      TFLOP/s of GEMM work (the same unit as the GPU value)."""
     import numpy as np
 
     import oracle
     import workloads
 
+    # quantizer sweep, full tensor
+    T = sweep_host if sweep_host is not None else workloads.SWEEP.generate()
+    b = qbytes(T.numel(), 2)
+    qsweep = {}
+    for axis in (1, 0):
+        for rnd in ("rne", "sr"):
+            for rht in (False, True):
+                t = time.perf_counter()
+                oracle.quantize(T, axis=axis, rounding=oracle.SR if rnd == "sr" else oracle.RNE, seed=seed,
+                                rht=rht, sign_mask=mask)
+                dt = time.perf_counter() - t
+                qsweep[f"axis{axis} {rnd}{'+rht' if rht else ''}"] = {"s": round(dt, 3),
+                                                                      "GB/s": round(b / dt / 1e9, 3)}
+    del T
+    # the step's quantizations in full, its GEMMs (fprop full, dgrad and
+    # wgrad on 512 output rows)
     t_q = 0.0
-    t_g = 0.0
+    gemms = {}
     rows_sample = 512
-    for g in (F, D, Wg):
+    for name, g in (("fprop", F), ("dgrad", D), ("wgrad", Wg)):
         refs = []
         for op in (g.a, g.b):
             x = op.generate()
@@ -704,16 +827,24 @@ def cpu_baseline(F, D, Wg, mask, seed, step_flops):
             t_q += time.perf_counter() - t
             del x
         m, n, k = g.mnk
-        rows = np.arange(rows_sample)
+        full = name == "fprop"
+        rows = None if full else np.arange(rows_sample)
         t = time.perf_counter()
         oracle.gemm(refs[0], refs[1], rows=rows)
-        t_g += (time.perf_counter() - t) * m / rows_sample
+        dt = time.perf_counter() - t
+        est = dt if full else dt * m / rows_sample
+        gemms[name] = {"s": round(est, 3), "TFLOP/s": round(g.flops / est / 1e12, 4),
+                       "measured": "full GEMM" if full else f"{rows_sample} of {m} output rows, extrapolated"}
+    t_g = sum(v["s"] for v in gemms.values())
     t_step = t_q + t_g
     return {"value": round(step_flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "cpu_model": cpu_model(), "kind": "oracle",
-            "sample": f"all six operand quantizations in full ({t_q:.1f}s) + oracle GEMM on {rows_sample} output "
-                      f"rows of each GEMM, extrapolated to the full M ({t_g:.1f}s est.); step {t_step:.1f}s",
-            "ms_per_step_est": round(t_step * 1e3, 1)}
+            "blas_threads": blas_threads(), "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"step: all six operand quantizations in full ({t_q:.1f}s) + the fprop oracle GEMM in full "
+                      f"and 512-row slices of dgrad and wgrad extrapolated to the full M ({t_g:.1f}s est.); "
+                      f"quantizer: all eight variants on the full 32768x8192 sweep tensor",
+            "ms_per_step_est": round(t_step * 1e3, 1),
+            "gemm": gemms,
+            "quantize_sweep_32768x8192_bf16": qsweep}
 
 
 if __name__ == "__main__":

@@ -47,7 +47,7 @@ _lib = None
 EXPORTS = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_quantize_dual",
            "mxfp4_quantize", "mxfp4_gemm", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_ws",
            "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_noalloc", "mxfp8_quantize", "mxfp8_gemm", "nvfp4_probe_mfma",
-           "nvfp4_status_string")
+           "nvfp4_probe_philox", "nvfp4_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemm_workspace_bytes.restype = i64
         L.nvfp4_probe_mfma.argtypes = [i64, vp, vp]
         L.nvfp4_probe_mfma.restype = ci
+        L.nvfp4_probe_philox.argtypes = [i64, vp, vp]
+        L.nvfp4_probe_philox.restype = ci
         L.nvfp4_status_string.argtypes = [ci]
         L.nvfp4_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -336,22 +338,26 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: tor
 _workspaces: dict = {}
 
 
-def gemm_workspace(device=None) -> torch.Tensor:
-    """The stream-K GEMM workspace of `device` (allocated zero-filled on
-    first use and kept: the kernel leaves it zero-filled).  Calls that share
-    it must not overlap in time, so it serves one stream at a time."""
+def gemm_workspace(device=None, stream=None) -> torch.Tensor:
+    """The split-tail GEMM workspace for one (device, stream): allocated
+    zero-filled on first use and kept (the kernel leaves it zero-filled).
+    Calls on one stream run in order, so a workspace per stream is never
+    used by two calls at once."""
     device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
-    ws = _workspaces.get(device)
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device, int(s.cuda_stream))
+    ws = _workspaces.get(key)
     if ws is None:
         ws = torch.zeros(int(lib().nvfp4_gemm_workspace_bytes()), dtype=torch.uint8, device=device)
-        _workspaces[device] = ws
+        _workspaces[key] = ws
     return ws
 
 
 def nvfp4_gemm_ws(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """C = A . B^T on the stream-K schedule (same result contract as
-    nvfp4_gemm); `workspace` defaults to the device's shared one."""
+    """C = A . B^T with a workspace (same result contract as nvfp4_gemm):
+    the tiles of a partly filled last round split into K ranges where that
+    is faster; `workspace` defaults to the one of (device, stream)."""
     code = _out_code(out_dtype)
     dev = a.device
     if b.device != dev:
@@ -359,7 +365,7 @@ def nvfp4_gemm_ws(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: 
     if out is None:
         out = torch.empty((a.outer, b.outer), dtype=out_dtype, device=dev)
     ldc = _require_matrix_out(out, a.outer, b.outer, out_dtype, dev)
-    ws = workspace if workspace is not None else gemm_workspace(dev)
+    ws = workspace if workspace is not None else gemm_workspace(dev, stream)
     _require_buffer(ws, "workspace", torch.uint8, int(lib().nvfp4_gemm_workspace_bytes()), dev)
     ca, cb = a._c(), b._c()
     with torch.cuda.device(dev):
@@ -400,6 +406,24 @@ def nvfp4_probe_mfma(iters: int, stream=None) -> float:
         e1.record(s)
     e1.synchronize()
     return 1024 * 4 * iters * 32 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
+def nvfp4_probe_philox(calls: int, stream=None) -> float:
+    """Run the Philox probe (include/nvfp4.h) once for `calls` counters on the
+    current device and return its time in ms (events on the probe's stream).
+    A measurement helper for the benchmark, not part of the method."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        _check(lib().nvfp4_probe_philox(min(calls, 1 << 20), out.data_ptr(), _stream_handle(s, dev)),
+               "nvfp4_probe_philox")
+        e0.record(s)
+        _check(lib().nvfp4_probe_philox(calls, out.data_ptr(), _stream_handle(s, dev)), "nvfp4_probe_philox")
+        e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1)
 
 
 class MXFP4Tensor:

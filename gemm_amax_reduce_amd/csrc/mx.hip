@@ -15,8 +15,9 @@
 // element block of its row (lane l: row l % 32, K half l / 32), measured
 // bit-exact against an fp64 reference: the codes feed the MFMA as they are,
 // with no decode, at the FP4 rate (64 K per 32-cycle instruction, four times
-// the f16 form's K).  (With FP8 operands the same instruction showed ~1e-4
-// relative rounding of the product sums, so only FP4 is offered.)
+// the f16 form's K).  (With FP8 operands the same instruction truncates its
+// products within groups of 8 K positions; MXFP8 is in mx8.hip with the
+// tolerance that follows from that.)
 #include "gemm_common.h"
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"

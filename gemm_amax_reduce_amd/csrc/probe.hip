@@ -58,8 +58,32 @@ k_probe_mfma(int64_t iters, float *out) {
   out[blockIdx.x * kProbeThreads + threadIdx.x] = t;
 }
 
+// The random bits of stochastic rounding alone: Philox4x32-10 (the same
+// device routine the encodes use) for counters 0 .. calls-1, one call per 8
+// elements, XOR-folded so the work stays live; no memory traffic besides one
+// word per thread.  Its time is the floor the RNG contract puts under every
+// stochastic-rounding encode of 8 * calls elements.
+__global__ void __launch_bounds__(kProbeThreads) k_probe_philox(int64_t calls, uint64_t seed, uint32_t *out) {
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < calls; i += stride) {
+    const uint4 w = sr_words8((uint64_t)i, seed, 0);
+    acc ^= w.x ^ w.y ^ w.z ^ w.w;
+  }
+  out[blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+
 }  // namespace
 }  // namespace nvfp4
+
+extern "C" int nvfp4_probe_philox(int64_t calls, uint32_t *out, void *hip_stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (calls < 0) return NVFP4_ERR_SHAPE;
+  if (((uintptr_t)out & 3) != 0) return NVFP4_ERR_ALIGN;
+  hipLaunchKernelGGL(nvfp4::k_probe_philox, dim3(nvfp4::kProbeBlocks * 4), dim3(nvfp4::kProbeThreads), 0,
+                     (hipStream_t)hip_stream, calls, (uint64_t)0x5EED, out);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
 
 extern "C" int nvfp4_probe_mfma(int64_t iters, float *out, void *hip_stream) {
   if (!out) return NVFP4_ERR_NULL;

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (nvfp4_gemm, nvfp4_quantize, nvfp4_quantize_dual, nvfp4_rht_quantize, NVFP4Error)
+from . import (nvfp4_gemm_ws, nvfp4_quantize, nvfp4_quantize_dual, nvfp4_rht_quantize, NVFP4Error)
 
 
 class NVFP4LinearFunction(torch.autograd.Function):
@@ -37,7 +37,7 @@ class NVFP4LinearFunction(torch.autograd.Function):
         qx = nvfp4_quantize(x, axis=1)
         qw = nvfp4_quantize(weight, axis=1)
         out_dtype = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
-        y = nvfp4_gemm(qx, qw, out_dtype)
+        y = nvfp4_gemm_ws(qx, qw, out_dtype)
         ctx.save_for_backward(x, weight)
         ctx.seed, ctx.offset, ctx.sign_mask = seed, offset, sign_mask
         return y
@@ -55,10 +55,10 @@ class NVFP4LinearFunction(torch.autograd.Function):
         dx = dw = None
         if ctx.needs_input_grad[0]:
             qw0 = nvfp4_quantize(weight, axis=0)
-            dx = nvfp4_gemm(qdy1, qw0, torch.float32).to(x.dtype)
+            dx = nvfp4_gemm_ws(qdy1, qw0, torch.float32).to(x.dtype)
         if ctx.needs_input_grad[1]:
             qx0 = nvfp4_rht_quantize(x, ctx.sign_mask, axis=0)
-            dw = nvfp4_gemm(qdy0, qx0, torch.float32).to(weight.dtype)
+            dw = nvfp4_gemm_ws(qdy0, qx0, torch.float32).to(weight.dtype)
         return dx, dw, None, None, None
 
 

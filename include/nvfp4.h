@@ -370,6 +370,17 @@ int mxfp8_gemm(const mxfp8_tensor *a, const mxfp8_tensor *b, void *c, int c_dtyp
  */
 int nvfp4_probe_mfma(int64_t iters, float *out, void *hip_stream);
 
+/*
+ * nvfp4_probe_philox -- measurement helper, not part of the method: runs the
+ * stochastic-rounding random generator alone (Philox4x32-10, the same
+ * routine the encodes use, counters 0 .. calls-1, one call per 8 elements)
+ * with no memory traffic, over 4096 workgroups of 256 threads, giving the
+ * floor the RNG contract puts under a stochastic-rounding encode of
+ * 8 * calls elements.  out: device, 4096 * 256 words (per-thread XOR of the
+ * outputs, which keeps the work live).
+ */
+int nvfp4_probe_philox(int64_t calls, uint32_t *out, void *hip_stream);
+
 /* Human-readable name of a status code (static string). */
 const char *nvfp4_status_string(int status);
 

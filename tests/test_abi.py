@@ -237,6 +237,9 @@ def test_probe_argument_errors(L):
     assert L.nvfp4_probe_mfma(10, None, None) == -1
     assert L.nvfp4_probe_mfma(-1, FAKE, None) == -2
     assert L.nvfp4_probe_mfma(10, FAKE + 2, None) == -5
+    assert L.nvfp4_probe_philox(10, None, None) == -1
+    assert L.nvfp4_probe_philox(-1, FAKE, None) == -2
+    assert L.nvfp4_probe_philox(10, FAKE + 2, None) == -5
 
 
 def test_bench_refuses_more_than_one_gpu():

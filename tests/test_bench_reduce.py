@@ -99,9 +99,13 @@ def test_busy_reduction(tmp_path):
                 "SQ_ACTIVE_INST_VALU": g * 1024 / 8, "SQ_INSTS_MFMA": 10.0, "SQ_INSTS_VALU": 60.0,
                 "SQ_WAIT_INST_ANY": g * 1024 / 16, "SQ_LDS_BANK_CONFLICT": g * 256 * 0.1}
     write_run(str(tmp_path / "b"), [("void nvfp4::k_gemm_nvfp4<true, true>(...)", 1, 1_000_000, counters),
+                                    ("void nvfp4::k_gemm_nvfp4_split<false, true>(...)", 1, 1_000_000, counters),
                                     ("void nvfp4::k_gemm_nvfp4<false, true>(...)", 1, 1_000_000, counters),
                                     ("void nvfp4::k_gemm_nvfp4<false, true>(...)", 1, 1_000_000, counters)])
     md = bench.reduce_busy(str(tmp_path / "b"))
+    rows = [line for line in md.splitlines() if line.startswith("| k_gemm")]
+    assert [r.split("|")[1].strip() for r in rows] == [
+        "k_gemm_nvfp4<true, true> (fprop)", "k_gemm_nvfp4_split<false, true> (dgrad)", "k_gemm_nvfp4<false, true> (wgrad)"]
     row = [c.strip() for c in md.splitlines()[-1].split("|")]
     # dispatches, ms, GHz, MFMA busy, VALU/MFMA, VALU active, issue wait, LDS conflict
     assert row[2:10] == ["2", "1.000", "2.00", "0.500", "6.00", "0.500", "0.250", "0.100"]
