@@ -78,8 +78,35 @@ def log(msg):
 # changed since, the traffic is reported as null.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_f32_dgrad_wgrad_traffic.json")
 GEMM_SOURCES = [os.path.join(ROOT, "gemm_amax_reduce_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h", "nvfp4_device.h")]
-DOMINANT = "k_gemm_nvfp4<false, true>"   # f32 output, scales by DMA (K % 64 == 0)
 CALIB_BYTES = 256 << 20
+MI355X_CUS = 256
+
+
+def gemm_launch(g, cus: int = MI355X_CUS):
+    """(kernel name, work-items) of the one launch nvfp4_gemm_ws makes for the
+    layer GEMM g: the stream-K kernel (grids of at least one round of 256 x
+    256 tiles, not a whole number of rounds, at least 16 K groups per tile),
+    all whole rounds but the last data-parallel plus one round of stream-K
+    workgroups, 256 threads each.  dgrad and wgrad share the f32-output
+    kernel and differ in grid size."""
+    m, n, k = g.mnk
+    tiles = -(-m // 256) * -(-n // 256)
+    ng = -(-k // 256)
+    p_sk = min(cus, 256) // 8 * 8
+    assert tiles >= p_sk and tiles % p_sk and ng >= 16 and k % 64 == 0, g.name
+    n_dp = (tiles // p_sk - 1) * p_sk
+    return "k_gemm_nvfp4_sk<%s, true>" % ("true" if g.out == "bf16" else "false"), (n_dp + p_sk) * 256
+
+
+def gemm_kinds():
+    import workloads
+    return [(name, gemm_launch(g)) for name, g in (("fprop", workloads.FPROP), ("dgrad", workloads.DGRAD),
+                                                   ("wgrad", workloads.WGRAD))]
+
+
+def dominant_launch():
+    """The dominant kernel: the one with the most time per step, wgrad's."""
+    return dict(gemm_kinds())["wgrad"]
 
 
 def gemm_source_hash() -> str:
@@ -110,6 +137,8 @@ def reduce_traffic(fetch_dir: str, write_dir: str) -> dict:
     import csv
     import glob
 
+    dom_name, dom_grid = dominant_launch()
+
     def per_kernel(d, counter):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         out = {}
@@ -118,7 +147,8 @@ def reduce_traffic(fetch_dir: str, write_dir: str) -> dict:
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                key = "dominant" if DOMINANT in name else "copy" if "copyBuffer" in name else None
+                dom = dom_name in name and int(r["Grid_Size"]) == dom_grid
+                key = "dominant" if dom else "copy" if "copyBuffer" in name else None
                 if key:
                     out.setdefault(key, []).append(float(r["Counter_Value"]))
         return out
@@ -136,7 +166,7 @@ def reduce_traffic(fetch_dir: str, write_dir: str) -> dict:
     w_scale = CALIB_BYTES / (w_copy * 1024.0)
     fetch_b = f_dom * 1024.0 * f_scale
     write_b = w_dom * 1024.0 * w_scale
-    return {"kernel": DOMINANT, "source_sha256": gemm_source_hash(),
+    return {"kernel": dom_name, "grid_work_items": dom_grid, "source_sha256": gemm_source_hash(),
             "fetch_kib_per_dispatch": f_dom, "write_kib_per_dispatch": w_dom,
             "calibration_copy_bytes": CALIB_BYTES, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
             "fetch_scale": f_scale, "write_scale": w_scale,
@@ -233,8 +263,7 @@ def reduce_busy(busy_dir: str) -> str:
     """MFMA busy fraction, clock and issue counters of the GEMM kernels from
     one rocprofv3 --pmc run of this script; returns the markdown summary."""
     ds = _dispatches(busy_dir)
-    kinds = (("k_gemm_nvfp4<true, true>", "fprop"), ("k_gemm_nvfp4_split<false, true>", "dgrad"),
-             ("k_gemm_nvfp4<false, true>", "wgrad"))
+    kinds = gemm_kinds()
     lines = ["# MFMA busy fraction and clock of the GEMM kernels (linear-layer step)", "",
              "Command (repository root, one MI355X; one counter pass, 7 SQ + 1 GRBM counters), then the reduction:",
              "", "```",
@@ -250,10 +279,10 @@ def reduce_busy(busy_dir: str) -> str:
              "the run (warm-up included).", "",
              "| kernel | dispatches | ms | clock GHz | MFMA busy | VALU instr / MFMA | VALU active | issue wait "
              "| LDS conflict cycles |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
-    for key, label in kinds:
-        sel = [e for e in ds if key in e[0]]
+    for label, (key, grid) in kinds:
+        sel = [e for e in ds if key in e[0] and e[1] == grid]
         if not sel:
-            raise SystemExit(f"--busy: no {key} dispatches in {busy_dir}")
+            raise SystemExit(f"--busy: no {key} dispatches of {grid} work-items in {busy_dir}")
         acc = {"ms": 0.0, "ghz": 0.0, "busy": 0.0, "ipm": 0.0, "va": 0.0, "wait": 0.0, "lds": 0.0}
         for e in sel:
             c, dur = e[4], (e[3] - e[2]) * 1e-9
@@ -467,11 +496,11 @@ def main():
         if release_after < i < first_wait:
             breakdown[ops[i][0]]["stream"] = "main, overlapped with the second stream's quantizations"
 
-    # dominant kernel: the one kernel with the most time per step, the
-    # f32-output data-parallel GEMM of wgrad (2*5120*20480*8192 flop per
-    # launch; dgrad's launch is the split kernel, fprop's the bf16 one); one
-    # GEMM call is one kernel launch on torch's current stream, which the
-    # events above are recorded on
+    # dominant kernel: the one kernel launch with the most time per step,
+    # wgrad's (2*5120*20480*8192 flop; f32-output stream-K kernel, as dgrad's
+    # but on a larger grid; fprop's is the bf16 one); one GEMM call is one
+    # kernel launch on torch's current stream, which the events above are
+    # recorded on
     gi = [i for i, (n, _, _) in enumerate(ops) if n == "gemm wgrad"]
     g_ms = float(np.mean(per_op[:, gi]))
     g_flop = Wg.flops
@@ -480,14 +509,12 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                 "traffic": round(traffic) if traffic else None,
-                "kernel": DOMINANT + " (f32 out, data-parallel grid): the wgrad launch of each step",
+                "kernel": "%s, %d work-items: the wgrad launch of each step" % dominant_launch(),
                 "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flop,
                 "algorithmic_bytes_per_launch": gemm_bytes(Wg),
                 "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4),
                 "frac_of_measured_mfma_probe": round(achieved / measured_peaks["mfma_f16_probe_TFLOP/s"], 4),
-                "gemm_kernels": {"fprop": "k_gemm_nvfp4<true, true> (bf16 out, mixed 256/128-wide grid)",
-                                 "dgrad": "k_gemm_nvfp4_split<false, true> (f32 out, tail split in two K ranges)",
-                                 "wgrad": DOMINANT + " (f32 out, mixed 256/128-wide grid)"}}
+                "gemm_kernels": {name: "%s, %d work-items (stream-K tail)" % launch for name, launch in gemm_kinds()}}
 
     # ------------------------------------------------ quantizer sweep ----
     sweep = None

@@ -78,12 +78,15 @@ template <int BN> using TileAcc = float16_t[4][BN / 64];
 // C[M][N] = A.B^T at rows m0.., columns n0.. (B, N already restricted to
 // this tile width's column range).  g1 > g0.  Every DMA this issues has
 // completed when it returns, so the LDS buffers are free again once all
-// waves are past a barrier.
+// waves are past a barrier.  With `flag` set, thread 0 stores 1 to it
+// once the prologue's wait has seen every earlier memory access of the
+// workgroup complete (the stores of a partial issued before the call).
 template <bool SCALE_DMA, int BN>
 __device__ __forceinline__ void tile_accumulate(uint8_t *smem, int64_t m0, int64_t n0, int g0, int g1,
                                                 const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
                                                 const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
-                                                int64_t M, int64_t N, int64_t K, TileAcc<BN> &acc) {
+                                                int64_t M, int64_t N, int64_t K, TileAcc<BN> &acc,
+                                                unsigned *flag = nullptr) {
   constexpr int NB = BN / 64;          // B fragments (32 columns each) per wave
   constexpr int NF = 4 + NB;           // operand fragments decoded per wave and K step
   constexpr int NU = 4 * NB;           // MFMAs per wave and K step
@@ -246,6 +249,7 @@ __device__ __forceinline__ void tile_accumulate(uint8_t *smem, int64_t m0, int64
   dma_part(g0 + 1, (g0 + 1) & 1, 3);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (flag != nullptr && tid == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   read_stage(0, smem + (g0 & 1) * kGroupBytes, g0, 0);
   __builtin_amdgcn_s_waitcnt(0);     // nothing outstanding at loop entry
   if constexpr (SCALE_DMA) pick_scales();
@@ -323,21 +327,67 @@ __device__ __forceinline__ void tile_accumulate(uint8_t *smem, int64_t m0, int64
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-// C tile = (acc * gA) * gB.  Lane holds column r and rows 8*(e/4) + 4*h +
-// e%4 of each 32x32 block; row offsets are uniform, so the per-store address
-// is one lane base plus a scalar offset.
+constexpr int kDeviceScope = 0x10;     // cache-policy bits: sc1
+
+// C tile = ((acc + P) * gA) * gB, P the unscaled f32 partial of a 256 x 256
+// tile at `partial` (workspace layout: float4 q of thread tid at byte
+// 16 * (256 q + tid)) or 0 when `partial` is null.  Lane holds column r and
+// rows 8*(e/4) + 4*h + e%4 of each 32x32 block; row offsets are uniform, so
+// the per-store address is one lane base plus a scalar offset.
+//
+// The partial goes through LDS, which must be free (every wave past the
+// main loop and a barrier): each half (blocks of rows i = 0,1, then 2,3) is
+// copied in by the DMA form -- all of a wave's loads in flight at once,
+// each wave only its own threads' float4s (1 KB per index q), so no barrier
+// between the copy and the reads -- and added block by block as the rows
+// are stored.  The loads use the sc1 policy (see store_partial_data).
 template <bool OUT_BF16, int BN>
 __device__ __forceinline__ void tile_store(const TileAcc<BN> &acc, int64_t m0, int64_t n0, float gA, float gB,
-                                           int64_t M, int64_t N, void *__restrict__ C, int64_t ldc) {
+                                           int64_t M, int64_t N, void *__restrict__ C, int64_t ldc,
+                                           int tid = threadIdx.x, uint8_t *smem = nullptr,
+                                           const uint8_t *partial = nullptr) {
   constexpr int NB = BN / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
   const int64_t row_l = m0 + wm * 128 + 4 * h, col_l = n0 + wn * (BN / 2) + r;
   const bool full_tile = (m0 + BM <= M) && (n0 + BN <= N);
   using OutT = typename std::conditional<OUT_BF16, uint16_t, float>::type;
   OutT *base = reinterpret_cast<OutT *>(C) + row_l * ldc + col_l;
+  __amdgpu_buffer_rsrc_t prsrc;
+  if (BN == 256 && partial != nullptr) prsrc = make_rsrc(partial, (uint32_t)(BM * 256 * 4));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float16_t v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) v[j] = acc[i][j];
+    if constexpr (BN == 256) {
+      if (partial != nullptr) {
+        if ((i & 1) == 0) {
+          // float4 q = 32 half + qq of every thread: 4 KB at 4096 q; this
+          // wave's kilobyte of it at + 1024 wave, into LDS at 4096 qq + the same
+          const int half = i >> 1;
+          __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the previous half's reads are done
+#pragma unroll
+          for (int qq = 0; qq < 32; ++qq)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                prsrc, (__attribute__((address_space(3))) void *)(smem + 4096 * qq + 1024 * wave), 16,
+                (uint32_t)(16 * lane), (uint32_t)(4096 * (32 * half + qq) + 1024 * wave), 0, kDeviceScope);
+          __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's copies are in LDS
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int b = (i & 1) * 4 + j;           // block (i, j) within its half
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 p = *reinterpret_cast<const float4 *>(smem + 4096 * (4 * b + q4) + 16 * tid);
+            v[j][4 * q4] += p.x;
+            v[j][4 * q4 + 1] += p.y;
+            v[j][4 * q4 + 2] += p.z;
+            v[j][4 * q4 + 3] += p.w;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int roff = 32 * i + 8 * (e >> 2) + (e & 3);
@@ -346,11 +396,11 @@ __device__ __forceinline__ void tile_store(const TileAcc<BN> &acc, int64_t m0, i
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (!full_tile && col_l + 32 * j >= N) continue;
-        const float v = (acc[i][j][e] * gA) * gB;
+        const float x = (v[j][e] * gA) * gB;
         if constexpr (OUT_BF16)
-          prow[32 * j] = f32_to_bf16_rne(v);
+          prow[32 * j] = f32_to_bf16_rne(x);
         else
-          prow[32 * j] = v;
+          prow[32 * j] = x;
       }
     }
   }
@@ -397,25 +447,23 @@ k_gemm_nvfp4(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
 // ------------------------------------------------------- split tail ----
 //
 // The data-parallel grid runs whole tiles, so when the tile count is not a
-// multiple of the CU count the last round leaves CUs idle (the layer shapes
-// have 320, 640 and 1600 tiles of 256 x 256 on 256 CUs: 1.25, 2.5 and 6.25
-// rounds).  Here the whole rounds run as before, and each of the remaining
-// `rem` tiles is cut into `sp` equal K ranges (sp = CUs / rem, at least
-// kMinSplitGroups K groups per range), one workgroup per range, so the last
-// round fills the CUs: 20 + 5, 2 x 80 + 40 and 6 x 32 + 8 group-times for
-// the three layers against 40, 240 and 224 with whole tiles.
+// multiple of the CU count the last round leaves CUs idle.  For grids of
+// fewer tiles than one round of the CUs (grids of at least one round take
+// the stream-K tail below): the whole rounds run as before, and each of
+// the remaining `rem` tiles is cut into `sp` equal K ranges (sp = CUs /
+// rem, at least kMinSplitGroups K groups per range), one workgroup per
+// range, so the CUs fill.
 //
 // Of the sp workgroups of a split tile, the last (highest-numbered) one
 // finishes it: the others each write their unscaled f32 partial to their
 // own workspace slot and raise its flag; the finisher waits for the flags,
 // adds the partials in increasing range order to its own, and stores the
 // tile.  The result does not depend on timing (deterministic).  Splitting
-// pays only where the tail's ranges are long or most CUs would otherwise
-// idle: measured on the layer shapes, dgrad (a 2-way split of 40-group
-// ranges) gains 1.5 %, while the 4-way splits of 5- and 8-group ranges of
-// fprop and wgrad lose 10 % and 1 % to the mixed 256/128-wide grid (a
-// second wave of short workgroups, each with its own prologue, partial and
-// wait), so the launcher takes that grid there.
+// the tail of a larger grid this way pays only where the ranges are long:
+// on the layer shapes, a 2-way split of dgrad's 40-group ranges gained
+// 1.5 %, 4-way splits of 5- and 8-group ranges (fprop, wgrad) lost 10 %
+// and 1 % to the mixed 256/128-wide grid (a second wave of short
+// workgroups, each with its own prologue, partial and wait).
 //
 // Progress: a finisher waits only for lower-numbered workgroups, which never
 // wait themselves; workgroups of one dispatch start in increasing order (per
@@ -457,6 +505,89 @@ __device__ __forceinline__ int xcd_logical(int pid, int n) {
   return (xcd < rq) ? xcd * (q + 1) + local : rq * (q + 1) + (xcd - rq) * q + local;
 }
 
+// Unscaled f32 partial of a 256 x 256 tile into a workspace slot, then the
+// slot's flag.  Float4 q of thread tid at byte 16 * (256 q + tid): each
+// wave's store or load instruction covers one contiguous kilobyte.  The
+// stores write through this XCD's L2 (the sc1 cache policy) and the flag
+// follows their completion, so a reader on another XCD that loads with the
+// same policy after seeing the flag gets the stored values.
+__device__ __forceinline__ void store_partial_data(const TileAcc<256> &acc, uint8_t *ws, int slot_idx) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t slot =
+      make_rsrc(ws + kSplitSlot0 + (int64_t)slot_idx * kSplitSlotBytes, (uint32_t)kSplitSlotBytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            (u32x4){__float_as_uint(acc[i][j][4 * c]), __float_as_uint(acc[i][j][4 * c + 1]),
+                    __float_as_uint(acc[i][j][4 * c + 2]), __float_as_uint(acc[i][j][4 * c + 3])},
+            slot, (uint32_t)(16 * (256 * ((i * 4 + j) * 4 + c) + tid)), 0, kDeviceScope);
+}
+
+__device__ __forceinline__ unsigned *slot_flag(uint8_t *ws, int slot_idx) {
+  return reinterpret_cast<unsigned *>(ws + (int64_t)slot_idx * kSplitFlagBytes);
+}
+
+// The partial and then its flag, once every wave's stores have completed.
+__device__ __forceinline__ void store_partial(const TileAcc<256> &acc, uint8_t *ws, int slot_idx) {
+  store_partial_data(acc, ws, slot_idx);
+  __builtin_amdgcn_s_waitcnt(0);     // this wave's partial stores have completed
+  __syncthreads();                   // ... and every other wave's
+  if (threadIdx.x == 0) __hip_atomic_store(slot_flag(ws, slot_idx), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (thread 0) for the flags of slots [c0, c1) and clear them; a wait
+// that gives up counts in the error word.  Ends with a workgroup barrier.
+__device__ __forceinline__ void wait_flags(uint8_t *ws, int c0, int c1) {
+  if (threadIdx.x == 0) {
+    for (int c = c0; c < c1; ++c) {
+      unsigned *flag = reinterpret_cast<unsigned *>(ws + (int64_t)c * kSplitFlagBytes);
+      unsigned n = 0;
+      while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (++n >= kSplitSpinLimit) {
+          atomicAdd(reinterpret_cast<unsigned *>(ws + kSplitErrOffset), 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
+// acc += the partials of slots c0 .. c0 + n - 1 (n not known at compile
+// time), in that order, one 32 x 32 block at a time: only that block's 16
+// accumulators pass through the loop over contributors (a loop carrying all
+// 256 would spill).
+__device__ __forceinline__ void add_partials_n(TileAcc<256> &acc, const uint8_t *ws, int c0, int n) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t parts =
+      make_rsrc(ws + kSplitSlot0 + (int64_t)c0 * kSplitSlotBytes, (uint32_t)(n * kSplitSlotBytes));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float16_t v = acc[i][j];
+      for (int c = 0; c < n; ++c) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(
+              parts, (uint32_t)(16 * (256 * ((i * 4 + j) * 4 + q) + tid)), (uint32_t)(c * kSplitSlotBytes),
+              kDeviceScope);
+          v[4 * q] += __uint_as_float(p.x);
+          v[4 * q + 1] += __uint_as_float(p.y);
+          v[4 * q + 2] += __uint_as_float(p.z);
+          v[4 * q + 3] += __uint_as_float(p.w);
+        }
+      }
+      acc[i][j] = v;
+    }
+}
+
 template <bool OUT_BF16, bool SCALE_DMA>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_gemm_nvfp4_split(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
@@ -464,7 +595,7 @@ k_gemm_nvfp4_split(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA
                    int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc, uint8_t *__restrict__ ws,
                    SplitSched sc) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kGroupBytes];
-  const int pid = blockIdx.x, tid = threadIdx.x;
+  const int pid = blockIdx.x;
   const int ng = (int)((K + kGroupK - 1) / kGroupK);
   int u, g0 = 0, g1 = ng, part = 0, t = 0;
   if (pid < sc.n_dp) {
@@ -481,77 +612,121 @@ k_gemm_nvfp4_split(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 256;
   TileAcc<256> acc;
   tile_accumulate<SCALE_DMA, 256>(smem, m0, n0, g0, g1, A, SA, B, SB, M, N, K, acc);
-  // Partial slot t holds float4 q of thread tid at byte 16 * (256 q + tid),
-  // so each wave's store or load instruction covers one contiguous
-  // kilobyte.  Partials are written and read with device-scope coherence
-  // (the sc1 cache policy: the stores write through this XCD's L2, the
-  // loads do not hit stale lines in the reader's), which makes them visible
-  // across XCDs once the stores have completed; the flag follows after
-  // the wait for completion.  (A release fence instead writes back the
-  // whole L2 of the XCD: measured 25 us slower on the fprop layer.)
-  constexpr int kDeviceScope = 0x10;     // cache-policy bits: sc1
-  const __amdgpu_buffer_rsrc_t slot = make_rsrc(ws + kSplitSlot0 + (int64_t)t * kSplitSlotBytes, (uint32_t)kSplitSlotBytes);
   if (pid >= sc.n_dp && part < sc.sp - 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          __builtin_amdgcn_raw_buffer_store_b128(
-              (u32x4){__float_as_uint(acc[i][j][4 * c]), __float_as_uint(acc[i][j][4 * c + 1]),
-                      __float_as_uint(acc[i][j][4 * c + 2]), __float_as_uint(acc[i][j][4 * c + 3])},
-              slot, (uint32_t)(16 * (256 * ((i * 4 + j) * 4 + c) + tid)), 0, kDeviceScope);
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's partial stores have completed
-    __syncthreads();                   // ... and every other wave's
-    if (tid == 0)
-      __hip_atomic_store(reinterpret_cast<unsigned *>(ws + (int64_t)t * kSplitFlagBytes), 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    store_partial(acc, ws, t);
     return;
   }
   if (pid >= sc.n_dp && sc.sp > 1) {
-    // the finisher: wait for ranges 0 .. sp-2 (slots t-part .. t-1), then
-    // add their partials one 32 x 32 block at a time (only that block's 16
-    // accumulators pass through the loop over contributors)
-    const int c0 = t - part;
-    if (tid == 0) {
-      for (int c = c0; c < t; ++c) {
-        unsigned *flag = reinterpret_cast<unsigned *>(ws + (int64_t)c * kSplitFlagBytes);
-        unsigned n = 0;
-        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-          if (++n >= kSplitSpinLimit) {
-            atomicAdd(reinterpret_cast<unsigned *>(ws + kSplitErrOffset), 1u);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(8);
-        }
-        __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-    const __amdgpu_buffer_rsrc_t parts =
-        make_rsrc(ws + kSplitSlot0 + (int64_t)c0 * kSplitSlotBytes, (uint32_t)(part * kSplitSlotBytes));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float16_t v = acc[i][j];
-        for (int c = 0; c < part; ++c) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(
-                parts, (uint32_t)(16 * (256 * ((i * 4 + j) * 4 + q) + tid)), (uint32_t)(c * kSplitSlotBytes),
-                kDeviceScope);
-            v[4 * q] += __uint_as_float(p.x);
-            v[4 * q + 1] += __uint_as_float(p.y);
-            v[4 * q + 2] += __uint_as_float(p.z);
-            v[4 * q + 3] += __uint_as_float(p.w);
-          }
-        }
-        acc[i][j] = v;
-      }
+    // the finisher: ranges 0 .. sp-2 are slots t-part .. t-1
+    wait_flags(ws, t - part, t);
+    add_partials_n(acc, ws, t - part, part);
   }
   tile_store<OUT_BF16, 256>(acc, m0, n0, metaA[1], metaB[1], M, N, C, ldc);
+}
+
+// ------------------------------------------------- stream-K tail ----
+//
+// For grids of at least one round of 256 x 256 tiles.  All rounds but the
+// last whole one run data-parallel (one tile per workgroup); the tiles left
+// (between one and two rounds) are cut into eight chunks of whole tiles, one
+// per XCD, and the chunk's K groups ("units", tile after tile in the grouped
+// tile order) are dealt out in equal contiguous ranges to the XCD's
+// workgroups.  Every range is at least one tile long, so a range is a head
+// segment (the first K groups of a tile, whose tail the next workgroup of
+// the XCD holds), whole tiles, and a tail segment (the rest of the tile
+// whose head the previous workgroup holds).  Each workgroup works its range
+// backwards: the head first -- its f32 partial goes to the workgroup's
+// workspace slot and raises its flag -- then the whole tiles, then the tail,
+// which it finishes by adding the previous workgroup's head partial (raised
+// long before) and storing the tile.  Every tile is thus the sum of at most
+// two ranges, added in one fixed order, and the last round fills the CUs:
+// the fprop, dgrad and wgrad layers (1.25, 2.5 and 6.25 rounds of work) run
+// it in as many round-times plus two segment starts.  Measured against the
+// mixed 256/128-wide grid on the same box: fprop -9.7 %, dgrad -1.6 % (as
+// the split tail), wgrad -0.8 % (that grid's partial last round of 256-wide
+// tiles already overlaps its 128-wide ones).  What keeps the overhead small:
+// the head's flag is raised by the next segment's prologue, whose wait for
+// its first DMA also covers the partial's stores; the tail adds the partial
+// from LDS, where each half of it arrives by DMA with all loads in flight
+// (loading it into registers block by block serialised 64 round trips to
+// memory and cost 9 % on fprop).
+//
+// Workgroups are dealt round-robin to the XCDs, so the XCD's workgroups are
+// pid = xcd + 8 l in increasing local index l, and a finisher waits only
+// for pid - 8 on its own XCD, which was dispatched before it and waits only
+// for pid - 16; the chain ends at l = 0, whose range starts a chunk.  The
+// wait is bounded as in the split kernel.  Workspace as for the split
+// kernel; slot and flag s belong to stream-K workgroup s (pid - n_dp).
+struct SkSched {
+  int tiles_m, tiles_n;     // 256 x 256 tiles of C, in row groups of kGroupM
+  int n_dp;                 // data-parallel tiles (the first n_dp), one workgroup each
+  int t_sk;                 // tiles of the stream-K part (the rest), t_sk >= 8 w
+  int w;                    // stream-K workgroups per XCD
+};
+
+template <bool OUT_BF16, bool SCALE_DMA>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_gemm_nvfp4_sk(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ metaA,
+                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ metaB,
+                int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc, uint8_t *__restrict__ ws,
+                SkSched sc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kGroupBytes];
+  const int pid = blockIdx.x;
+  const int ng = (int)((K + kGroupK - 1) / kGroupK);
+  // this workgroup's units [v0, v1), unit v = K group v % ng of tile v / ng
+  // (tiles * ng < 2^31, checked by the launcher)
+  int v0, v1;
+  int s = -1;                        // stream-K index (slot), -1 if data-parallel
+  if (pid < sc.n_dp) {
+    v0 = xcd_logical(pid, sc.n_dp) * ng;
+    v1 = v0 + ng;
+  } else {
+    s = pid - sc.n_dp;
+    const int xcd = s % 8, l = s / 8;
+    const int c0 = (int)((int64_t)sc.t_sk * xcd / 8), c1 = (int)((int64_t)sc.t_sk * (xcd + 1) / 8);
+    const int base = (sc.n_dp + c0) * ng;
+    const int64_t units = (int64_t)(c1 - c0) * ng;
+    v0 = base + (int)(units * l / sc.w);
+    v1 = base + (int)(units * (l + 1) / sc.w);
+  }
+  const int t_hi = (v1 - 1) / ng, g_hi = v1 - t_hi * ng;     // last tile, its end group (1 .. ng)
+  const int t_lo = v0 / ng, g_lo = v0 - t_lo * ng;           // first tile, its start group
+  int t = t_hi;
+  if (g_hi < ng) {
+    // head segment (groups [0, g_hi) of tile t_hi): the next workgroup of
+    // the XCD finishes the tile
+    int tm, tn;
+    grouped_tile(t, sc.tiles_m, sc.tiles_n, tm, tn);
+    TileAcc<256> acc;
+    tile_accumulate<SCALE_DMA, 256>(smem, (int64_t)tm * BM, (int64_t)tn * 256, 0, g_hi, A, SA, B, SB, M, N, K, acc);
+    // the flag is raised by the next segment once these stores complete
+    store_partial_data(acc, ws, s);
+    --t;
+  }
+  unsigned *flag = g_hi < ng ? slot_flag(ws, s) : nullptr;
+  const float gA = metaA[1], gB = metaB[1];
+  for (; t >= t_lo; --t) {
+    const int g0 = t == t_lo ? g_lo : 0;
+    if (t != t_hi || g_hi < ng) __syncthreads();    // every wave is done with the previous segment's LDS
+    int tm, tn;
+    grouped_tile(t, sc.tiles_m, sc.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 256;
+    TileAcc<256> acc;
+    tile_accumulate<SCALE_DMA, 256>(smem, m0, n0, g0, ng, A, SA, B, SB, M, N, K, acc, flag);
+    flag = nullptr;
+    // Opaque copies of what only the epilogue uses: keeps the compiler from
+    // computing the epilogue's addressing before the loop and holding it in
+    // registers across the main loop.
+    int64_t ldc_s = ldc, m_s = M, n_s = N;
+    int tid = threadIdx.x;
+    asm volatile("" : "+s"(ldc_s), "+s"(m_s), "+s"(n_s), "+v"(tid));
+    const uint8_t *partial = nullptr;
+    if (g0 > 0) {                    // tail: add the head of the previous workgroup of the XCD
+      wait_flags(ws, s - 8, s - 7);
+      partial = ws + kSplitSlot0 + (int64_t)(s - 8) * kSplitSlotBytes;
+    }
+    tile_store<OUT_BF16, 256>(acc, m0, n0, gA, gB, m_s, n_s, C, ldc_s, tid, smem, partial);
+  }
 }
 
 __global__ void k_zero_c(void *C, int64_t M, int64_t N, int64_t ldc, int elem) {
@@ -690,6 +865,36 @@ hipError_t launch_gemm_split(const uint8_t *a_codes, const uint8_t *a_scales, co
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + 255) / 256, tiles = tiles_m * tiles_n;
   const int64_t ng = (K + kGroupK - 1) / kGroupK;
   const int64_t P = std::min<int64_t>(device_cus(), kSplitMaxSlots);
+  const bool scale_dma = K % 64 == 0;
+  // At least one round of tiles, not a whole number of rounds: the
+  // stream-K tail over the last one to two rounds, on P rounded down to
+  // whole XCDs, when tiles are long enough in K that a segment's start and
+  // the partial's round trip are small against it (measured: at 8 groups
+  // per tile the stream-K tail is 10 % slower than the mixed grid, at 20
+  // and more it is faster).
+  constexpr int64_t kSkMinGroups = 16;
+  const int64_t p_sk = P / 8 * 8;
+  if (p_sk >= 8 && tiles >= p_sk && tiles % p_sk != 0 && ng >= kSkMinGroups && tiles * ng <= INT32_MAX) {
+    SkSched sk;
+    sk.tiles_m = (int)tiles_m;
+    sk.tiles_n = (int)tiles_n;
+    sk.n_dp = (int)((tiles / p_sk - 1) * p_sk);
+    sk.t_sk = (int)(tiles - sk.n_dp);
+    sk.w = (int)(p_sk / 8);
+    const dim3 grid((unsigned)(sk.n_dp + p_sk));
+#define NVFP4_GEMM_SK_LAUNCH(OB, SD)                                                                               \
+  hipLaunchKernelGGL((k_gemm_nvfp4_sk<OB, SD>), grid, dim3(kThreads), 0, stream, a_codes, a_scales, a_meta, b_codes, \
+                     b_scales, b_meta, M, N, K, c, ldc, (uint8_t *)ws, sk)
+    if (c_dtype == 0) {
+      if (scale_dma) NVFP4_GEMM_SK_LAUNCH(false, true);
+      else NVFP4_GEMM_SK_LAUNCH(false, false);
+    } else {
+      if (scale_dma) NVFP4_GEMM_SK_LAUNCH(true, true);
+      else NVFP4_GEMM_SK_LAUNCH(true, false);
+    }
+#undef NVFP4_GEMM_SK_LAUNCH
+    return hipGetLastError();
+  }
   // whole rounds data-parallel; the rem remaining tiles split into sp K
   // ranges each, sp * rem <= P, at least kMinSplitGroups groups per range.
   // The split is taken when most CUs would idle without it (fewer than P/2
@@ -707,7 +912,6 @@ hipError_t launch_gemm_split(const uint8_t *a_codes, const uint8_t *a_scales, co
   sc.tiles_n = (int)tiles_n;
   sc.n_dp = (int)(tiles - rem);
   sc.sp = (int)sp;
-  const bool scale_dma = K % 64 == 0;
 #define NVFP4_GEMM_SPLIT_LAUNCH(OB, SD)                                                                         \
   hipLaunchKernelGGL((k_gemm_nvfp4_split<OB, SD>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a_codes,     \
                      a_scales, a_meta, b_codes, b_scales, b_meta, M, N, K, c, ldc, (uint8_t *)ws, sc)

@@ -226,19 +226,28 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
 
 /*
  * nvfp4_gemm_ws -- nvfp4_gemm with a caller-owned workspace, which lets it
- * split the tiles of the last, partly filled round of the CUs into K ranges
- * (split tail).  The data-parallel grid runs whole 256 x 256 output tiles,
- * so when the tile count is not a multiple of the CU count the last round
- * leaves CUs idle.  Here whole rounds run as before and each remaining tile
- * is cut into up to CUs / tiles-left-over K ranges, one workgroup each; the
- * workgroup of the last range adds the others' f32 partials (kept in the
- * workspace) in a fixed order -- deterministic, no atomics on the data.
- * The split is taken where it is faster: when fewer than half the CUs would
- * get a tile, or when the ranges stay long (at least 4096 K positions);
- * otherwise the call runs nvfp4_gemm's grid.  Same operands, output and
- * accuracy contract as nvfp4_gemm; a split shortens each f32 accumulation
- * chain (the partials then add in binary32), which keeps same-sign
- * operands inside the tolerance at any K when the output has few tiles.
+ * balance the last, partly filled round of the CUs by splitting tiles along
+ * K.  The data-parallel grid runs whole 256 x 256 output tiles, so when the
+ * tile count is not a multiple of the CU count the last round leaves CUs
+ * idle.  Two schedules use the workspace:
+ *  - stream-K tail (at least one round of tiles, not a whole number of
+ *    rounds, at least 4096 K positions per tile): all whole rounds but the
+ *    last run data-parallel; the remaining tiles' K groups are dealt out in
+ *    equal contiguous ranges to one round of workgroups, eight chunks (one
+ *    per XCD) of whole tiles.  A tile is then the sum of at most two
+ *    ranges: the workgroup holding its end adds the f32 partial of the one
+ *    holding its start (kept in the workspace).
+ *  - split tail (fewer tiles than one round): whole rounds run as before and
+ *    each remaining tile is cut into up to CUs / tiles-left-over K ranges;
+ *    the workgroup of the last range adds the others' partials.  Taken when
+ *    fewer than half the CUs would get a tile or the ranges stay long (at
+ *    least 4096 K positions).
+ * Otherwise the call runs nvfp4_gemm's grid.  Partials add in a fixed order
+ * -- deterministic for a given device, no atomics on the data.  Same
+ * operands, output and accuracy contract as nvfp4_gemm; a split shortens
+ * each f32 accumulation chain (the partials then add in binary32), which
+ * keeps same-sign operands inside the tolerance at any K when the output
+ * has few tiles.
  *  workspace       : device, at least nvfp4_gemm_workspace_bytes() bytes,
  *                    256-byte aligned, zero-filled before its FIRST use (the
  *                    kernel leaves it zero-filled again when it completes,

@@ -80,12 +80,25 @@ def test_quant_counter_order_is_checked(tmp_path):
         bench.reduce_quant_counters(str(tmp_path / "fetch"), str(tmp_path / "write"), str(tmp_path / "valu"))
 
 
+def test_gemm_launches():
+    """The layer GEMMs' stream-K grids on 256 CUs: 320, 640 and 1600 tiles
+    leave 0, 256 and 1280 data-parallel tiles plus one round."""
+    kinds = dict(bench.gemm_kinds())
+    assert kinds["fprop"] == ("k_gemm_nvfp4_sk<true, true>", 256 * 256)
+    assert kinds["dgrad"] == ("k_gemm_nvfp4_sk<false, true>", 512 * 256)
+    assert kinds["wgrad"] == ("k_gemm_nvfp4_sk<false, true>", 1536 * 256)
+    assert bench.dominant_launch() == kinds["wgrad"]
+
+
 def test_traffic_reduction(tmp_path):
     kib = bench.CALIB_BYTES / 1024
-    dom = f"void nvfp4::{bench.DOMINANT}(...)"
-    write_run(str(tmp_path / "f"), [(COPY, 1, 100, {"FETCH_SIZE": 2 * kib}), (dom, 1, 100, {"FETCH_SIZE": 1000.0}),
-                                    (dom, 1, 100, {"FETCH_SIZE": 3000.0})])
-    write_run(str(tmp_path / "w"), [(COPY, 1, 100, {"WRITE_SIZE": kib}), (dom, 1, 100, {"WRITE_SIZE": 500.0})])
+    name, grid = bench.dominant_launch()
+    dom = f"void nvfp4::{name}(...)"
+    # dgrad's launch of the same kernel (smaller grid) is not counted
+    write_run(str(tmp_path / "f"), [(COPY, 1, 100, {"FETCH_SIZE": 2 * kib}), (dom, grid, 100, {"FETCH_SIZE": 1000.0}),
+                                    (dom, 512 * 256, 100, {"FETCH_SIZE": 7.0}),
+                                    (dom, grid, 100, {"FETCH_SIZE": 3000.0})])
+    write_run(str(tmp_path / "w"), [(COPY, 1, 100, {"WRITE_SIZE": kib}), (dom, grid, 100, {"WRITE_SIZE": 500.0})])
     prof = bench.reduce_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
     assert prof["fetch_scale"] == pytest.approx(0.5) and prof["write_scale"] == pytest.approx(1.0)
     assert prof["fetch_bytes_per_launch"] == pytest.approx(2000 * 1024 * 0.5)
@@ -98,14 +111,16 @@ def test_busy_reduction(tmp_path):
     counters = {"GRBM_GUI_ACTIVE": 8 * g, "SQ_VALU_MFMA_BUSY_CYCLES": g * 1024 * 0.5, "SQ_BUSY_CYCLES": 1.0,
                 "SQ_ACTIVE_INST_VALU": g * 1024 / 8, "SQ_INSTS_MFMA": 10.0, "SQ_INSTS_VALU": 60.0,
                 "SQ_WAIT_INST_ANY": g * 1024 / 16, "SQ_LDS_BANK_CONFLICT": g * 256 * 0.1}
-    write_run(str(tmp_path / "b"), [("void nvfp4::k_gemm_nvfp4<true, true>(...)", 1, 1_000_000, counters),
-                                    ("void nvfp4::k_gemm_nvfp4_split<false, true>(...)", 1, 1_000_000, counters),
-                                    ("void nvfp4::k_gemm_nvfp4<false, true>(...)", 1, 1_000_000, counters),
-                                    ("void nvfp4::k_gemm_nvfp4<false, true>(...)", 1, 1_000_000, counters)])
+    f32 = "void nvfp4::k_gemm_nvfp4_sk<false, true>(...)"
+    write_run(str(tmp_path / "b"), [("void nvfp4::k_gemm_nvfp4_sk<true, true>(...)", 256 * 256, 1_000_000, counters),
+                                    (f32, 512 * 256, 1_000_000, counters),
+                                    (f32, 1536 * 256, 1_000_000, counters),
+                                    (f32, 1536 * 256, 1_000_000, counters)])
     md = bench.reduce_busy(str(tmp_path / "b"))
     rows = [line for line in md.splitlines() if line.startswith("| k_gemm")]
     assert [r.split("|")[1].strip() for r in rows] == [
-        "k_gemm_nvfp4<true, true> (fprop)", "k_gemm_nvfp4_split<false, true> (dgrad)", "k_gemm_nvfp4<false, true> (wgrad)"]
+        "k_gemm_nvfp4_sk<true, true> (fprop)", "k_gemm_nvfp4_sk<false, true> (dgrad)",
+        "k_gemm_nvfp4_sk<false, true> (wgrad)"]
     row = [c.strip() for c in md.splitlines()[-1].split("|")]
     # dispatches, ms, GHz, MFMA busy, VALU/MFMA, VALU active, issue wait, LDS conflict
     assert row[2:10] == ["2", "1.000", "2.00", "0.500", "6.00", "0.500", "0.250", "0.100"]

@@ -2,16 +2,18 @@
 float64 oracle, and the accuracy of both GEMM entry points on same-sign
 operands.
 
-nvfp4_gemm_ws runs whole rounds of 256 x 256 tiles data-parallel and cuts
-each tile left over into equal K ranges whose f32 partials are added in a
-fixed order through the caller's workspace (when that is faster; otherwise
-it runs nvfp4_gemm's grid).  Shapes here take every branch: few tiles split
-up to the per-range minimum (1, 4 and 6 tiles), the tail of a larger grid
-split 2 ways (4600 x 5120 x 8192: 360 tiles, 104 left over, ragged M), no
-split (too few K groups, or short ranges), K % 64 != 0 (per-lane scale
-loads), f32 and bf16 output, and the three layer shapes.  Tolerance as for
-nvfp4_gemm: every element within 1e-5 * gA gB sum_k |(qA SA)(qB SB)| of the
-oracle.
+nvfp4_gemm_ws balances the last round of 256 x 256 tiles through the
+caller's workspace: grids of at least one round take the stream-K tail
+(the last one to two rounds' K groups dealt out in equal ranges; a tile is
+the sum of at most two ranges), smaller grids the split tail (each tile
+left over cut into equal K ranges), and the rest nvfp4_gemm's grid.  Shapes
+here take every branch: few tiles split up to the per-range minimum (1, 4
+and 6 tiles), stream-K on a ragged grid (4600 x 5120 x 8192: 360 tiles)
+and on a ragged grid with K % 64 != 0 (4200 x 4000 x 4112: 272 tiles, per-
+lane scale loads), the mixed grid (340 tiles of 8 K groups: too short for
+stream-K; 20 tiles of 4 groups: too short to split), f32 and bf16 output,
+and the three layer shapes (all stream-K).  Tolerance as for nvfp4_gemm:
+every element within 1e-5 * gA gB sum_k |(qA SA)(qB SB)| of the oracle.
 """
 import functools
 
@@ -87,10 +89,12 @@ def ws():
 
 # (m, n, k): 1 tile K=4096 (split 4); 4 tiles K=5120 (split 5); 6 tiles
 # K=2064 (K % 64 != 0, split 2); 20 tiles K=1024 (4 groups: no split); 360
-# tiles K=8192 (104 left over, split 2, ragged M); 340 tiles K=2048 (short
-# ranges: the mixed grid); small ragged shapes; one element
+# tiles K=8192 (stream-K, ragged M); 272 tiles K=4112 (stream-K, ragged M
+# and N, K % 64 != 0); 340 tiles K=2048 (8 groups: the mixed grid); small
+# ragged shapes; one element
 SHAPES = [(256, 256, 4096), (512, 512, 5120), (300, 700, 2064), (1024, 1280, 1024),
-          (4600, 5120, 8192), (4352, 5120, 2048), (200, 136, 272), (257, 129, 16), (3, 517, 48), (1, 1, 16)]
+          (4600, 5120, 8192), (4200, 4000, 4112), (4352, 5120, 2048), (200, 136, 272), (257, 129, 16), (3, 517, 48),
+          (1, 1, 16)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -108,11 +112,12 @@ def test_split_shapes(ws, m, n, k, out):
     _workspace_clean(ws)
 
 
-def test_deterministic_and_reusable(ws):
-    """Bit-identical results over repeated calls with one workspace (the
-    split tiles add their partials in a fixed order), the workspace clean
-    after each."""
-    ra, rb = _rand_q(512, 5120, 63), _rand_q(512, 5120, 64)
+@pytest.mark.parametrize("m,n,k", [(512, 512, 5120), (4600, 5120, 8192)])
+def test_deterministic_and_reusable(ws, m, n, k):
+    """Bit-identical results over repeated calls with one workspace (split
+    and stream-K tiles add their partials in a fixed order), the workspace
+    clean after each."""
+    ra, rb = _rand_q(m, k, 63), _rand_q(n, k, 64)
     qa, qb = _upload(ra), _upload(rb)
     first = _gemm_ws(qa, qb, "f32", ws)
     for _ in range(3):
@@ -122,10 +127,9 @@ def test_deterministic_and_reusable(ws):
 
 @pytest.mark.parametrize("name", ["fprop", "dgrad", "wgrad"])
 def test_layer_shapes(ws, name):
-    """The three layer GEMMs (dgrad takes the split: 640 tiles, the 128
-    left over cut in two 40-group ranges; fprop and wgrad the mixed grid) on
-    the oracle's operands, sampled rows and columns (every tile position)
-    against the oracle."""
+    """The three layer GEMMs (all three take the stream-K tail: 320, 640 and
+    1600 tiles) on the oracle's operands, sampled rows and columns (every
+    tile position) against the oracle."""
     g = workloads.GEMMS[name]
     mask = workloads.rht_sign_mask()
     refs = []
