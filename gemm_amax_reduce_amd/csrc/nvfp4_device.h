@@ -110,35 +110,37 @@ __device__ __forceinline__ uint32_t encode8_rne(const float *v) {
 // the exact rational rule on 3.8 M (value, rand) pairs covering every
 // binade, the saturation at 6, signs and tiny values), so rand =
 // (r16 << 16) | 0x8000 gives the rule above.  The second value of a pair
-// sees rand << 1, which would tie neighbouring elements' random bits, so
-// each conversion carries one element with +0 as its partner: byte 0 of the
-// result is then the element's code (the partner's code 0 in the high
-// nibble).  Only byte 0 is used -- the compiler does not keep the other
-// bytes of the destination -- and v_perm_b32 gathers the codes.
-__device__ __forceinline__ uint32_t sr_code_byte(float v, uint32_t rand) {
-  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (float2_t){v, 0.0f}, rand, 1.0f, 0);
-}
-
-// Byte 0 of a, b, c, d -> bytes 0..3 of the result.
-__device__ __forceinline__ uint32_t gather_byte0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);   // [a0, b0, 0, 0]
-  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000C0Cu);   // [0, 0, c0, d0]
-  return ab | cd;
-}
-
-// Four Philox words w[0..3] carry the 16-bit draws of elements 0..7
-// (element 2j: low half of w[j], element 2j+1: high half).  Returns the
-// eight stochastically rounded codes of v[0..7], element 0 lowest.
+// rounds with rand << 1 (checked bit for bit against the first-value form
+// on 16.8 M (value, r16) cases), so one conversion of the pair (v[2j],
+// v[2j+1]) with rand = R_even gives the even element's code in the low
+// nibble, and one with rand = R_odd >> 1 (R_odd has bit 0 clear) the odd
+// element's code in the high nibble; the other nibble of each is unused.
+// Eight conversions, each writing one byte of a word (byte sel, the other
+// bytes kept), build the even and odd words; one masked merge gives the 8
+// codes.  Written as one asm block: the compiler's form of the byte-select
+// conversion does not keep the destination's other bytes.  The two chains
+// alternate, so no conversion reads a result of the instruction just before.
 __device__ __forceinline__ uint32_t encode8_sr(const float *v, const uint32_t *w) {
-  uint32_t c[8];
+  const float2_t p0 = {v[0], v[1]}, p1 = {v[2], v[3]}, p2 = {v[4], v[5]}, p3 = {v[6], v[7]};
+  uint32_t re[4], ro[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    c[2 * j] = sr_code_byte(v[2 * j], (w[j] << 16) | 0x8000u);
-    c[2 * j + 1] = sr_code_byte(v[2 * j + 1], (w[j] & 0xFFFF0000u) | 0x8000u);
+    re[j] = (w[j] << 16) | 0x8000u;
+    ro[j] = ((w[j] >> 1) & 0x7FFF8000u) | 0x4000u;     // ((w & 0xFFFF0000) | 0x8000) >> 1
   }
-  const uint32_t ev = gather_byte0(c[0], c[2], c[4], c[6]);
-  const uint32_t od = gather_byte0(c[1], c[3], c[5], c[7]);
-  return ev | (od << 4);
+  uint32_t ev, od;
+  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %2, %6, 1.0\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %2, %10, 1.0\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %3, %7, 1.0 op_sel:[0,0,1,0]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %3, %11, 1.0 op_sel:[0,0,1,0]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %4, %8, 1.0 op_sel:[0,0,0,1]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %4, %12, 1.0 op_sel:[0,0,0,1]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %5, %9, 1.0 op_sel:[0,0,1,1]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %5, %13, 1.0 op_sel:[0,0,1,1]"
+      : "=&v"(ev), "=&v"(od)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(re[0]), "v"(re[1]), "v"(re[2]), "v"(re[3]), "v"(ro[0]),
+        "v"(ro[1]), "v"(ro[2]), "v"(ro[3]));
+  return (ev & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
 }
 
 // -------------------------------------------------------------- Philox ----
@@ -223,6 +225,22 @@ __device__ __forceinline__ TensorScales tensor_scales(float amax) {
 __device__ __forceinline__ uint32_t block_scale(uint32_t bmax_bits, const TensorScales &ts, float *m) {
   uint32_t S = e4m3_rne_sat(__uint_as_float(bmax_bits) * ts.k);
   *m = (S == 0u) ? 0.0f : __fdiv_rn(ts.s_enc, e4m3_to_f32(S));
+  return S;
+}
+
+// The element multiplier of every block scale code (0 for code 0, codes
+// past 0x7E unused): the same correctly rounded quotients block_scale
+// computes, one division per code and workgroup instead of one per block.
+// Threads [t0, t0 + 128) fill it; the caller puts a barrier before any use.
+__device__ __forceinline__ void fill_scale_lut(float *lut, const TensorScales &ts, int t0) {
+  const int i = (int)threadIdx.x - t0;
+  if (i >= 0 && i < 128) lut[i] = (i == 0 || i > 0x7E) ? 0.0f : __fdiv_rn(ts.s_enc, e4m3_to_f32((uint32_t)i));
+}
+
+__device__ __forceinline__ uint32_t block_scale_lut(uint32_t bmax_bits, const TensorScales &ts, const float *lut,
+                                                    float *m) {
+  const uint32_t S = e4m3_rne_sat(__uint_as_float(bmax_bits) * ts.k);
+  *m = lut[S];
   return S;
 }
 

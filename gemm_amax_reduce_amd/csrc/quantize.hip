@@ -290,6 +290,13 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
   const float amax = meta[0];
   const TensorScales ts = tensor_scales(amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) meta[1] = ts.g;
+  // stochastic rounding walks several blocks per thread: their multipliers
+  // come from a per-workgroup table
+  __shared__ float lut[128];
+  if constexpr (SR) {
+    fill_scale_lut(lut, ts, 0);
+    __syncthreads();
+  }
   const int64_t stride = (int64_t)gridDim.x * kQT;
   for (int64_t i = (int64_t)blockIdx.x * kQT + threadIdx.x; i < nblocks; i += stride) {
     const int64_t b = nblocks - 1 - i;
@@ -297,7 +304,7 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
     Load16<T>::run(x + 16 * b, y);
     if (RHT) rht16(y, sign_mask);
     float m;
-    uint32_t S = block_scale(absmax_bits16(y), ts, &m);
+    uint32_t S = SR ? block_scale_lut(absmax_bits16(y), ts, lut, &m) : block_scale(absmax_bits16(y), ts, &m);
     codes[b] = encode16<SR>(y, m, (uint64_t)b, seed, offset);
     scales[b] = (uint8_t)S;
   }
@@ -319,6 +326,9 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
   // before it is written back (pieces from different workgroups, possibly on
   // different XCDs, left L2 as partial lines: +25-45 % HBM write bytes).
   static_assert(kQT == 256, "four waves per workgroup");
+  __shared__ float lut[128];         // multipliers of the block scale codes
+  fill_scale_lut(lut, ts, 0);
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c = ((int64_t)(gridDim.x - 1 - blockIdx.x) * 64 + lane) * CPT;
   const int64_t nkb = rows / 16, kb0 = ((int64_t)(gridDim.y - 1 - blockIdx.y) * 4 + wave) * kNBT;
@@ -336,7 +346,7 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
     for (int e = 0; e < CPT; ++e) {
       if (RHT) rht16(y[e], sign_mask);
       float m;
-      const uint32_t S = block_scale(absmax_bits16(y[e]), ts, &m);
+      const uint32_t S = block_scale_lut(absmax_bits16(y[e]), ts, lut, &m);
       const int64_t blk = (c + e) * nkb + kb0 + i;   // block index in the [outer][K/16] layout
       cw[e][i] = encode16<SR>(y[e], m, (uint64_t)blk, seed, offset);
       sc[e] |= S << (8 * i);
@@ -493,6 +503,11 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
     meta1[1] = ts1.g;
     meta0[1] = ts0.g;
   }
+  // multipliers of the block scale codes of each layout (the staging
+  // barrier below orders these writes before their reads)
+  __shared__ float lut1[128], lut0[128];
+  fill_scale_lut(lut1, ts1, 0);
+  fill_scale_lut(lut0, ts0, 128);
   // ---- stage the tile (rows past `rows` and chunks past `cols` skipped:
   // no block that reads them is encoded)
   constexpr int kChunksRow = kDualCols / E;
@@ -522,7 +537,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
 #pragma unroll
       for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(src[j]);
       float m;
-      const uint32_t S = block_scale(absmax_bits16(y), ts1, &m);
+      const uint32_t S = block_scale_lut(absmax_bits16(y), ts1, lut1, &m);
       cw[i] = encode16<SR1>(y, m, (uint64_t)(gr * nb1 + gc / 16), seed1, offset1);
       sc |= S << (8 * i);
       nvalid = i + 1;
@@ -560,7 +575,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
       for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(*reinterpret_cast<const T *>(tile + (16 * i + j) * kPitch + t * (int)sizeof(T)));
       if (RHT0) rht16(y, sign_mask0);
       float m;
-      const uint32_t S = block_scale(absmax_bits16(y), ts0, &m);
+      const uint32_t S = block_scale_lut(absmax_bits16(y), ts0, lut0, &m);
       cw[i] = encode16<SR0>(y, m, (uint64_t)(gc * nb0 + gr / 16), seed0, offset0);
       sc |= S << (8 * i);
       nvalid = i + 1;
