@@ -39,6 +39,27 @@ constexpr int kQT = kQuantThreads;
 // aligned: output buffers need only the alignment of their element type.
 __device__ __forceinline__ bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Streaming (non-temporal) stores for outputs written as contiguous runs:
+// the lines are not kept in the caches ahead of the input still to be read.
+// Measured on the 32768 x 8192 bf16 tensor: the axis-1 quantizations 5-6 %
+// faster; the axis-0 ones, whose output is 128-byte lines 16 KB apart, 7 %
+// slower, so those keep ordinary stores.
+typedef unsigned nt_u2 __attribute__((ext_vector_type(2)));
+typedef unsigned nt_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(uint2 *p, uint2 v) {
+  __builtin_nontemporal_store((nt_u2){v.x, v.y}, reinterpret_cast<nt_u2 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v) {
+  __builtin_nontemporal_store((nt_u4){v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u4 *>(p));
+}
+__device__ __forceinline__ void store_nt(float4 *p, float4 v) {
+  __builtin_nontemporal_store((nt_u4){__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                      __float_as_uint(v.w)},
+                              reinterpret_cast<nt_u4 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(uint8_t *p, uint8_t v) { __builtin_nontemporal_store(v, p); }
+
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
@@ -305,8 +326,8 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
     if (RHT) rht16(y, sign_mask);
     float m;
     uint32_t S = SR ? block_scale_lut(absmax_bits16(y), ts, lut, &m) : block_scale(absmax_bits16(y), ts, &m);
-    codes[b] = encode16<SR>(y, m, (uint64_t)b, seed, offset);
-    scales[b] = (uint8_t)S;
+    store_nt(codes + b, encode16<SR>(y, m, (uint64_t)b, seed, offset));
+    store_nt(scales + b, (uint8_t)S);
   }
 }
 
@@ -412,38 +433,28 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
 
 // ---------------------------------------------------------- dequantize ----
 
-// bf16 output: one thread per 16-block (32 bytes of output in two 16-byte
-// stores); value = (e2m1 * S) * g in f32, rounded once to bf16.
-__global__ void __launch_bounds__(kQT) k_dequant_bf16(const uint2 *codes, const uint8_t *scales, const float *meta,
-                                                     int64_t nblocks, uint16_t *y) {
+// bf16 output: one thread per half block (8 elements, one 16-byte store),
+// so the lanes of a wave store one contiguous 1 KB run per instruction;
+// value = (e2m1 * S) * g in f32, rounded once to bf16.
+__global__ void __launch_bounds__(kQT) k_dequant_bf16(const uint32_t *codes, const uint8_t *scales, const float *meta,
+                                                     int64_t nhalves, uint16_t *y) {
   const float g = meta[1];
   const int64_t stride = (int64_t)gridDim.x * kQT;
-  for (int64_t b = (int64_t)blockIdx.x * kQT + threadIdx.x; b < nblocks; b += stride) {
-    uint2 c = codes[b];
-    float S = e4m3_to_f32(scales[b]);
-    float v[16];
-    uint32_t w[2] = {c.x, c.y};
+  for (int64_t q = (int64_t)blockIdx.x * kQT + threadIdx.x; q < nhalves; q += stride) {
+    const uint32_t w = codes[q];           // elements 8(q%2) .. +7 of block q/2: 4 code bytes
+    const float S = e4m3_to_f32(scales[q >> 1]);
+    uint32_t o[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t nib = (w[h] >> (4 * j)) & 15u;
-        half2_t q = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 0);
-        v[8 * h + j] = ((float)q[0] * S) * g;
-      }
-    }
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w >> (8 * i)) & 15u, 1.0f, 0);
+      const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w >> (8 * i + 4)) & 15u, 1.0f, 0);
       // nearest-even bf16 of each f32 (NaN cannot occur for finite meta)
-      uint32_t lo = __float_as_uint(v[2 * i]), hi = __float_as_uint(v[2 * i + 1]);
-      lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
-      hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-      o[i] = lo | (hi << 16);
+      uint32_t a = __float_as_uint(((float)lo[0] * S) * g), c = __float_as_uint(((float)hi[0] * S) * g);
+      a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
+      c = (c + 0x7FFFu + ((c >> 16) & 1u)) >> 16;
+      o[i] = a | (c << 16);
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(y + 16 * b);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    store_nt(reinterpret_cast<uint4 *>(y + 8 * q), make_uint4(o[0], o[1], o[2], o[3]));
   }
 }
 
@@ -464,7 +475,7 @@ __global__ void __launch_bounds__(kQT) k_dequant_f32(const uint16_t *codes, cons
       const half2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w >> (4 * j)) & 15u, 1.0f, 0);
       v[j] = ((float)h[0] * S) * g;
     }
-    *reinterpret_cast<float4 *>(y + 4 * q) = make_float4(v[0], v[1], v[2], v[3]);
+    store_nt(reinterpret_cast<float4 *>(y + 4 * q), make_float4(v[0], v[1], v[2], v[3]));
   }
 }
 
@@ -545,15 +556,15 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
     const int64_t b = gr * nb1 + (c0 / 16 + cb0);
     if (nvalid == 4 && aligned_to(codes1 + b, 16)) {
       uint4 *dst = reinterpret_cast<uint4 *>(codes1 + b);
-      dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
-      dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
+      store_nt(dst, make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y));
+      store_nt(dst + 1, make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i < nvalid) codes1[b + i] = cw[i];
     }
     if (nvalid == 4 && aligned_to(scales1 + b, 4)) {
-      *reinterpret_cast<uint32_t *>(scales1 + b) = sc;
+      store_nt(reinterpret_cast<uint32_t *>(scales1 + b), sc);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -773,8 +784,8 @@ hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const 
     hipLaunchKernelGGL(k_dequant_f32, dim3(grid_for(4 * nblocks)), dim3(kQT), 0, stream, (const uint16_t *)codes,
                        scales, meta, 4 * nblocks, (float *)y);
   else
-    hipLaunchKernelGGL(k_dequant_bf16, dim3(grid_for(nblocks)), dim3(kQT), 0, stream, (const uint2 *)codes, scales,
-                       meta, nblocks, (uint16_t *)y);
+    hipLaunchKernelGGL(k_dequant_bf16, dim3(grid_for(2 * nblocks)), dim3(kQT), 0, stream, (const uint32_t *)codes,
+                       scales, meta, 2 * nblocks, (uint16_t *)y);
   return hipGetLastError();
 }
 
