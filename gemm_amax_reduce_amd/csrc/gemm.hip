@@ -396,11 +396,13 @@ __device__ __forceinline__ void tile_store(const TileAcc<BN> &acc, int64_t m0, i
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (!full_tile && col_l + 32 * j >= N) continue;
+        // streaming stores: C is written once, and its lines would
+        // otherwise take cache space from the operand panels
         const float x = (v[j][e] * gA) * gB;
         if constexpr (OUT_BF16)
-          prow[32 * j] = f32_to_bf16_rne(x);
+          __builtin_nontemporal_store(f32_to_bf16_rne(x), prow + 32 * j);
         else
-          prow[32 * j] = x;
+          __builtin_nontemporal_store(x, prow + 32 * j);
       }
     }
   }

@@ -284,9 +284,9 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
       for (int j = 0; j < NB; ++j) {
         if (!full_tile && col_l + 32 * j >= N) continue;
         if constexpr (OUT_BF16)
-          prow[32 * j] = f32_to_bf16_rne(acc[i][j][e]);
+          __builtin_nontemporal_store(f32_to_bf16_rne(acc[i][j][e]), prow + 32 * j);   // streaming: C is written once
         else
-          prow[32 * j] = acc[i][j][e];
+          __builtin_nontemporal_store(acc[i][j][e], prow + 32 * j);
       }
     }
   }
