@@ -54,9 +54,9 @@ def qbytes(n_elem: int, in_bytes: int) -> int:
 
 def qbytes_dual(n_elem: int, in_bytes: int) -> int:
     """Algorithmic HBM bytes of a dual-layout quantization: the input is read
-    three times (one amax pass, two encode passes), two sets of codes and
-    scales written."""
-    return n_elem * (3 * in_bytes) + 2 * (n_elem // 2 + n_elem // 16)
+    twice (the amax pass, then one encode pass that writes both layouts), two
+    sets of codes and scales written."""
+    return n_elem * (2 * in_bytes) + 2 * (n_elem // 2 + n_elem // 16)
 
 
 def gemm_bytes(g) -> int:
@@ -76,7 +76,8 @@ def log(msg):
 # of known size that every run performs (CALIB_BYTES, outside the timed
 # region).  The profile records a hash of the kernel sources; when they have
 # changed since, the traffic is reported as null.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_f32_dgrad_wgrad_traffic.json")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_wgrad_5120x20480x8192_traffic.json")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_wgrad_5120x20480x8192_traffic.md")
 GEMM_SOURCES = [os.path.join(ROOT, "gemm_amax_reduce_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h", "nvfp4_device.h")]
 CALIB_BYTES = 256 << 20
 MI355X_CUS = 256
@@ -193,26 +194,143 @@ def _dispatches(d):
     return [disp[k] for k in sorted(disp)]
 
 
-def reduce_quant_counters(fetch_dir: str, write_dir: str, valu_dir: str) -> str:
+TRACE_PROFILE = os.path.join(ROOT, "profiles", "linear_layer_step_and_sweep_kernel_trace.md")
+def _trace_rows(d):
+    """Kernel dispatches of a rocprofv3 --kernel-trace run in start order:
+    [(name, work-items, start_ns, end_ns)]."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    out = []
+    for fn in files:
+        for r in csv.DictReader(open(fn)):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            out.append((r["Kernel_Name"], grid, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out.sort(key=lambda e: e[2])
+    return out
+
+
+def _sweep_sequence(ds, what):
+    """The quantizer sweep's dispatches (meta init, amax, encode per call,
+    SWEEP_CALLS calls per variant in SWEEP_VARIANTS order), checked."""
+    n = 32768 * 8192
+    first = next(i for i, e in enumerate(ds) if "k_quant_rows<unsigned short, false, false>" in e[0] and e[1] == n // 16)
+    seq = ds[first - 2: first - 2 + 3 * SWEEP_CALLS * len(SWEEP_VARIANTS)]
+    for v, (axis, rnd, rht) in enumerate(SWEEP_VARIANTS):
+        amax = "k_amax_rht_" + ("rows" if axis else "cols") if rht else "k_amax_flat"
+        enc = "k_quant_%s<unsigned short, %s, %s>" % ("rows" if axis else "cols", str(rnd == "sr").lower(),
+                                                      str(rht).lower())
+        for c in range(SWEEP_CALLS):
+            trio = seq[3 * (v * SWEEP_CALLS + c): 3 * (v * SWEEP_CALLS + c) + 3]
+            if len(trio) < 3 or not ("k_meta_init" in trio[0][0] and amax in trio[1][0] and enc in trio[2][0]):
+                raise SystemExit(f"{what}: unexpected dispatch order at variant {v} call {c}")
+    return seq
+
+
+def _short(name: str) -> str:
+    import re
+    m = re.search(r"(k_\w+(<[^()]*>)?)", name)
+    if m and "nvfp4" in name:
+        return m.group(1)
+    if "Cijk" in name or "gemm" in name.lower() and "nvfp4" not in name:
+        return "library GEMM (" + name.split("(")[0][:48] + ")"
+    return name.split("(")[0].replace("void ", "")[:70]
+
+
+def reduce_trace(trace_dir: str, bench_json: str) -> str:
+    """The kernel-trace profile of one bench run: per-kernel statistics, the
+    GEMM launches of the timed steps against the bench line's own event
+    timing, and the quantizer sweep's passes."""
+    import csv
+    import glob
+    with open(bench_json) as f:
+        line = [l for l in f.read().splitlines() if l.strip().startswith("{")][-1]
+    b = json.loads(line)
+    ds = _trace_rows(trace_dir)
+    steps, warmup = b["steps"], b["warmup"]
+    out = ["# Kernel trace: linear-layer step + 32768x8192 quantizer sweep", "",
+           "Commands (repository root, one MI355X): the bench run under the tracer, its JSON line kept, then "
+           "the reduction:", "", "```",
+           f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o bench --output-format csv -- python3 bench.py "
+           f"--steps {steps} --warmup {warmup} --no-cpu-baseline > {bench_json}",
+           f"python3 bench.py --trace {trace_dir} {bench_json}", "```", "",
+           f"Bench line of this run: value {b['value']} {b['unit']}, {b['ms_per_step']} ms per step "
+           f"({steps} timed steps after {warmup} warm-up; the tracer slows the step).", ""]
+    # GEMM launches
+    out += ["## GEMM launches", "",
+            "Each layer GEMM is one `nvfp4_gemm_ws` launch, identified by kernel and grid size. The last "
+            f"{steps} launches of each are the timed steps'.", "",
+            "| GEMM | kernel | work-items | launches | trace avg of timed ms | min | max | bench events ms | "
+            "TFLOP/s (trace) | of 2.5 PF/s |", "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    import workloads
+    gemms = {"fprop": workloads.FPROP, "dgrad": workloads.DGRAD, "wgrad": workloads.WGRAD}
+    bd = b.get("breakdown", {})
+    dom = None
+    for name, (kern, grid) in gemm_kinds():
+        launches = [(e[3] - e[2]) / 1e6 for e in ds if kern in e[0] and e[1] == grid]
+        if len(launches) < steps:
+            raise SystemExit(f"--trace: {len(launches)} launches of {kern} ({grid}) < {steps} steps")
+        t = launches[-steps:]
+        avg = sum(t) / len(t)
+        tf = gemms[name].flops / (avg * 1e-3) / 1e12
+        ev = bd.get("gemm " + name, {}).get("ms")
+        out.append(f"| {name} | `{kern}` | {grid} | {len(launches)} | {avg:.4f} | {min(t):.4f} | {max(t):.4f} | "
+                   f"{ev} | {tf:.1f} | {tf / PEAK_F16_TFLOPS:.4f} |")
+        if name == "wgrad":
+            dom = (avg, tf)
+    rf = b.get("roofline", {})
+    out += ["", f"Dominant kernel (wgrad's launch): the bench line reports `avg_launch_ms` {rf.get('avg_launch_ms')} "
+            f"and `frac` {rf.get('frac')} from its HIP events; the trace average of the same {steps} launches is "
+            f"{dom[0]:.4f} ms, i.e. frac {dom[1] / PEAK_F16_TFLOPS:.4f}.", ""]
+    # quantizer sweep
+    if b.get("quantize_sweep_32768x8192_bf16"):
+        seq = _sweep_sequence(ds, "--trace")
+        sw = b["quantize_sweep_32768x8192_bf16"]
+        n = 32768 * 8192
+        alg = 2 * n * 2 + n // 2 + n // 16
+        out += ["## Quantizer sweep (32768x8192 bf16)", "",
+                f"Per call: meta init, amax pass, encode pass. Trace averages over calls 3-{SWEEP_CALLS} of each "
+                "variant (the bench times the same calls with events around each call).", "",
+                "| variant | amax kernel us | encode kernel us | sum of the 3 kernels us | bench call us | "
+                "GB/s (alg. 4.5625 B/elem, trace sum) |", "|---|---:|---:|---:|---:|---:|"]
+        for v, (axis, rnd, rht) in enumerate(SWEEP_VARIANTS):
+            calls = [seq[3 * (v * SWEEP_CALLS + c): 3 * (v * SWEEP_CALLS + c) + 3] for c in range(2, SWEEP_CALLS)]
+            am = sum((c[1][3] - c[1][2]) for c in calls) / len(calls) / 1e3
+            en = sum((c[2][3] - c[2][2]) for c in calls) / len(calls) / 1e3
+            tot = sum(sum(e[3] - e[2] for e in c) for c in calls) / len(calls) / 1e3
+            key = f"axis{axis} {rnd}{'+rht' if rht else ''}"
+            bms = sw.get(key, {}).get("ms")
+            out.append(f"| {key} | {am:.1f} | {en:.1f} | {tot:.1f} | {bms * 1e3 if bms else float('nan'):.1f} | "
+                       f"{alg / (tot * 1e-6) / 1e9:.0f} |")
+        out.append("")
+    # per-kernel statistics
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        rows = list(csv.DictReader(open(stats[0])))
+        rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        out += ["## Per-kernel statistics (the whole run, warm-up and context sections included)", "",
+                "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+        for r in rows[:30]:
+            out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                       f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                       f"{float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def reduce_quant_counters(fetch_dir: str, write_dir: str, valu_dir: str, trace_dir: str) -> str:
     """Per-pass HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by the calibration
-    copy), time and VALU busy of the quantizer sweep's calls, from three
-    rocprofv3 --pmc runs of this script; returns the markdown summary."""
+    copy), VALU busy and clock of the quantizer sweep's calls from three
+    rocprofv3 --pmc runs of this script, and their times from a kernel-trace
+    run (counter collection serialises dispatches, and the chip clocks
+    differently between them); returns the markdown summary."""
     n = 32768 * 8192
     runs = {}
     for tag, d in (("fetch", fetch_dir), ("write", write_dir), ("valu", valu_dir)):
         ds = _dispatches(d)
-        first = next(i for i, e in enumerate(ds)
-                     if "k_quant_rows<unsigned short, false, false>" in e[0] and e[1] == n // 16)
-        seq = ds[first - 2: first - 2 + 3 * SWEEP_CALLS * len(SWEEP_VARIANTS)]
-        for v, (axis, rnd, rht) in enumerate(SWEEP_VARIANTS):
-            amax = "k_amax_rht_" + ("rows" if axis else "cols") if rht else "k_amax_flat"
-            enc = "k_quant_%s<unsigned short, %s, %s>" % ("rows" if axis else "cols", str(rnd == "sr").lower(),
-                                                          str(rht).lower())
-            for c in range(SWEEP_CALLS):
-                trio = seq[3 * (v * SWEEP_CALLS + c): 3 * (v * SWEEP_CALLS + c) + 3]
-                if not ("k_meta_init" in trio[0][0] and amax in trio[1][0] and enc in trio[2][0]):
-                    raise SystemExit(f"--quant-counters: unexpected dispatch order in {d} at variant {v} call {c}")
-        runs[tag] = (ds, seq)
+        runs[tag] = (ds, _sweep_sequence(ds, f"--quant-counters ({d})"))
+    trace_seq = _sweep_sequence(_trace_rows(trace_dir), f"--quant-counters ({trace_dir})")
     copies = [e for e in runs["fetch"][0] if "copyBuffer" in e[0]]
     f_scale = CALIB_BYTES / (max(e[4]["FETCH_SIZE"] for e in copies) * 1024.0)
     copies = [e for e in runs["write"][0] if "copyBuffer" in e[0]]
@@ -225,12 +343,16 @@ def reduce_quant_counters(fetch_dir: str, write_dir: str, valu_dir: str) -> str:
             fe = [runs["fetch"][1][i] for i in idx]
             we = [runs["write"][1][i] for i in idx]
             va = [runs["valu"][1][i] for i in idx]
-            us = sum((e[3] - e[2]) / 1e3 for e in fe) / len(fe)
+            te = [trace_seq[i] for i in idx]
+            us = sum((e[3] - e[2]) / 1e3 for e in te) / len(te)               # kernel trace
+            us_pmc = sum((e[3] - e[2]) / 1e3 for e in va) / len(va)          # counter run
             rd = sum(e[4]["FETCH_SIZE"] for e in fe) / len(fe) * 1024.0 * f_scale
             wr = sum(e[4]["WRITE_SIZE"] for e in we) / len(we) * 1024.0 * w_scale
             busy = sum(e[4]["SQ_INSTS_VALU"] * 4 / (e[4]["GRBM_GUI_ACTIVE"] / 8 * 1024) for e in va) / len(va)
+            ghz = sum(e[4]["GRBM_GUI_ACTIVE"] / 8 / (e[3] - e[2]) for e in va) / len(va)
             rows.append((f"axis{axis} {rnd}{'+rht' if rht else ''}", pname, fe[0][0].split("::")[-1].split("(")[0],
-                         us, rd, alg_read, wr, alg_write if p == 2 else 0, (rd + wr) / (us * 1e-6) / 1e9, busy))
+                         us, rd, alg_read, wr, alg_write if p == 2 else 0, (rd + wr) / (us * 1e-6) / 1e9, busy,
+                         us_pmc, ghz))
     run = "--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline"
     lines = ["# Quantizer counters on the 32768x8192 bf16 sweep tensor", "",
              "Commands (repository root, one MI355X), one counter set per run, then the reduction:", "", "```",
@@ -238,23 +360,53 @@ def reduce_quant_counters(fetch_dir: str, write_dir: str, valu_dir: str) -> str:
              f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -d {write_dir} -o run {run}",
              f"rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR "
              f"--kernel-trace -d {valu_dir} -o run {run}",
-             f"python3 bench.py --quant-counters {fetch_dir} {write_dir} {valu_dir}", "```", "",
+             f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o run {run}",
+             f"python3 bench.py --quant-counters {fetch_dir} {write_dir} {valu_dir} {trace_dir}", "```", "",
              f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for the 256 MiB "
              f"calibration copy of the same run ({f_scale:.2f} and {w_scale:.2f}). The tensor (512 MiB) exceeds the "
              "256 MB MALL. Algorithmic bytes per call: the amax pass reads 537 MB; the encode pass reads 537 MB and "
              "writes 151 MB of codes and scales. VALU busy = SQ_INSTS_VALU x 4 cycles / (GRBM_GUI_ACTIVE/8 x 1024 "
              "SIMDs), the share of SIMD issue cycles spent on VALU instructions at one pass each (quarter-rate "
-             "instructions such as the 64-bit multiplies of Philox take four, so SR is undercounted). Times from "
-             f"the FETCH_SIZE run's dispatch timestamps. Averages over the {SWEEP_CALLS} calls of each variant.", "",
-             "| variant | pass | kernel | us | HBM read MB (alg.) | HBM write MB (alg.) | achieved GB/s | VALU busy |",
-             "|---|---|---|---:|---:|---:|---:|---:|"]
-    for (var, pname, kern, us, rd, ard, wr, awr, gbs, busy) in rows:
+             "instructions such as the 64-bit multiplies of Philox take more, so SR is undercounted). Times (and "
+             "GB/s) from the kernel-trace run; the counter run's own dispatch time and clock (GRBM_GUI_ACTIVE/8 "
+             "over that time) beside them: counter collection serialises the dispatches, and the chip runs them "
+             f"at another clock. Averages over the {SWEEP_CALLS} calls of each variant.", "",
+             "| variant | pass | kernel | us (trace) | HBM read MB (alg.) | HBM write MB (alg.) | achieved GB/s | "
+             "VALU busy | us (counter run) | clock GHz (counter run) |",
+             "|---|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (var, pname, kern, us, rd, ard, wr, awr, gbs, busy, us_pmc, ghz) in rows:
         lines.append(f"| {var} | {pname} | {kern} | {us:.1f} | {rd / 1e6:.0f} ({ard / 1e6:.0f}) | "
-                     f"{wr / 1e6:.0f} ({awr / 1e6:.0f}) | {gbs:.0f} | {busy:.2f} |")
+                     f"{wr / 1e6:.0f} ({awr / 1e6:.0f}) | {gbs:.0f} | {busy:.2f} | {us_pmc:.1f} | {ghz:.2f} |")
     return "\n".join(lines) + "\n"
 
 
-BUSY_PROFILE = os.path.join(ROOT, "profiles", "gemm_f32_dgrad_wgrad_mfma_busy.md")
+def traffic_summary(prof: dict) -> str:
+    """Markdown summary of the traffic profile of the dominant kernel."""
+    import workloads
+    g = workloads.WGRAD
+    m, n, k = g.mnk
+    alg_r = (m + n) * k * 9 // 16
+    alg_w = m * n * 4
+    fb, wb = prof["fetch_bytes_per_launch"], prof["write_bytes_per_launch"]
+    return "\n".join([
+        f"# HBM-side traffic of `{prof['kernel']}` ({prof['grid_work_items']} work-items: the wgrad GEMM "
+        f"{m}x{n}x{k})", "",
+        "Commands (repository root, one MI355X), each counter in a run of its own, then the reduction:", "",
+        "```", *prof["command"].split(" && "), "```", "",
+        f"Calibration: every bench run copies a 256 MiB f32 tensor once (`__amd_rocclr_copyBuffer`, outside the "
+        f"timed region); that copy read {prof['copy_fetch_kib']:.0f} KiB by FETCH_SIZE and wrote "
+        f"{prof['copy_write_kib']:.0f} KiB by WRITE_SIZE for 262144 KiB moved each way, so FETCH_SIZE is scaled by "
+        f"{prof['fetch_scale']:.2f} and WRITE_SIZE by {prof['write_scale']:.2f}. Dispatches averaged: "
+        f"{prof['dispatches'][0]} (FETCH_SIZE run), {prof['dispatches'][1]} (WRITE_SIZE run). The profile holds the "
+        "SHA-256 of the GEMM sources it was taken on; the bench reports `traffic` only while they match.", "",
+        "| per launch | counter (KiB) | scaled bytes | algorithmic bytes |", "|---|---:|---:|---:|",
+        f"| read | {prof['fetch_kib_per_dispatch']:.0f} | {fb / 1e6:.0f} MB | {alg_r / 1e6:.0f} MB (codes + scales of A "
+        "and B once) |",
+        f"| write | {prof['write_kib_per_dispatch']:.0f} | {wb / 1e6:.0f} MB | {alg_w / 1e6:.0f} MB (f32 C once) |",
+        f"| total | | **{(fb + wb) / 1e6:.0f} MB** | **{(alg_r + alg_w) / 1e6:.0f} MB** |", ""])
+
+
+BUSY_PROFILE = os.path.join(ROOT, "profiles", "gemm_fprop_dgrad_wgrad_mfma_busy.md")
 BUSY_COUNTERS = ("GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA "
                  "SQ_INSTS_VALU SQ_WAIT_INST_ANY SQ_LDS_BANK_CONFLICT")
 
@@ -310,9 +462,12 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="reduce two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script into "
                          "the traffic profile and exit (no GPU needed)")
-    ap.add_argument("--quant-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "VALU_DIR"),
+    ap.add_argument("--quant-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "VALU_DIR", "TRACE_DIR"),
                     help="reduce three rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE, VALU counters) "
-                         "into the quantizer counter profile and exit (no GPU needed)")
+                         "and one kernel-trace run into the quantizer counter profile and exit (no GPU needed)")
+    ap.add_argument("--trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="reduce a rocprofv3 --kernel-trace --stats run of this script (and the JSON line it "
+                         "printed) into the kernel-trace profile and exit (no GPU needed)")
     ap.add_argument("--busy", metavar="BUSY_DIR",
                     help="reduce a rocprofv3 --pmc run of this script with the MFMA-busy counters into the GEMM "
                          "busy profile and exit (no GPU needed)")
@@ -320,6 +475,12 @@ def main():
     if args.busy:
         md = reduce_busy(args.busy)
         with open(BUSY_PROFILE, "w") as f:
+            f.write(md)
+        print(md)
+        return
+    if args.trace:
+        md = reduce_trace(*args.trace)
+        with open(TRACE_PROFILE, "w") as f:
             f.write(md)
         print(md)
         return
@@ -337,7 +498,10 @@ def main():
                            f"python3 bench.py --traffic {args.traffic[0]} {args.traffic[1]}")
         with open(TRAFFIC_PROFILE, "w") as f:
             json.dump(prof, f, indent=1)
-        print(json.dumps(prof))
+        md = traffic_summary(prof)
+        with open(TRAFFIC_SUMMARY, "w") as f:
+            f.write(md)
+        print(md)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",

@@ -30,6 +30,32 @@ def write_run(d, dispatches):
             t += dur + 10
 
 
+TRACE_FIELDS = ["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id", "Kernel_Name",
+                "Correlation_Id", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+                "Accum_VGPR_Count", "SGPR_Count", "Workgroup_Size_X", "Workgroup_Size_Y", "Workgroup_Size_Z",
+                "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+
+
+def write_trace(d, dispatches, stats=None):
+    """dispatches: [(name, work_items, duration_ns)] in order; stats: kernel_stats rows."""
+    os.makedirs(d, exist_ok=True)
+    t = 1000
+    with open(os.path.join(d, "run_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=TRACE_FIELDS)
+        w.writeheader()
+        for i, (name, grid, dur) in enumerate(dispatches, start=1):
+            w.writerow({**{k: 1 for k in TRACE_FIELDS}, "Dispatch_Id": i, "Kernel_Name": name, "Start_Timestamp": t,
+                        "End_Timestamp": t + dur, "Grid_Size_X": grid, "Grid_Size_Y": 1, "Grid_Size_Z": 1})
+            t += dur + 10
+    if stats:
+        with open(os.path.join(d, "run_kernel_stats.csv"), "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                                              "MaxNs", "StdDev"])
+            w.writeheader()
+            for r in stats:
+                w.writerow(r)
+
+
 def sweep_dispatches(counters_of):
     out = []
     for axis, rnd, rht in bench.SWEEP_VARIANTS:
@@ -54,18 +80,29 @@ def test_quant_counter_table(tmp_path):
         disp += [(n, g, dur, {cname: 1.0}) for n, g, dur, _ in step]
         disp += sweep_dispatches(lambda kind: {cname: per[kind]})
         write_run(str(tmp_path / tag), disp)
+    # VALU run: 2e5 GPU cycles per dispatch (GRBM_GUI_ACTIVE counts 8 XCDs), half the SIMD cycles on VALU
+    g = 2.0e5
     valu = [(COPY, 1, 100000, {"GRBM_GUI_ACTIVE": 8.0, "SQ_INSTS_VALU": 0.0})]
-    valu += sweep_dispatches(lambda kind: {"GRBM_GUI_ACTIVE": 8.0 * 1000, "SQ_INSTS_VALU": 1024 * 1000 / 4 / 2})
+    valu += sweep_dispatches(lambda kind: {"GRBM_GUI_ACTIVE": 8.0 * g, "SQ_INSTS_VALU": 0.5 * g * 1024 / 4})
     write_run(str(tmp_path / "valu"), valu)
-    md = bench.reduce_quant_counters(str(tmp_path / "fetch"), str(tmp_path / "write"), str(tmp_path / "valu"))
+    # kernel-trace run: the encodes take 120 us there (110 us in the counter runs)
+    trace = [(n, g_, 120000 if "k_quant" in n else dur) for n, g_, dur, _ in sweep_dispatches(lambda kind: {})]
+    write_trace(str(tmp_path / "trace"), [("void nvfp4::k_quant_rows<unsigned short, false, false>(...)",
+                                           4096 * 5120 // 16, 30000)] + trace)
+    md = bench.reduce_quant_counters(str(tmp_path / "fetch"), str(tmp_path / "write"), str(tmp_path / "valu"),
+                                     str(tmp_path / "trace"))
     rows = [l for l in md.splitlines() if l.startswith("| axis")]
     assert len(rows) == 2 * len(bench.SWEEP_VARIANTS)
-    first_enc = rows[1].split("|")
-    assert first_enc[2].strip() == "encode" and "k_quant_rows<unsigned short, false, false>" in first_enc[3]
-    assert first_enc[4].strip() == "110.0"                         # us from the timestamps
-    assert first_enc[5].strip() == "537 (537)"                      # 2 B/element read, scaled by 0.5
-    assert first_enc[6].strip() == "151 (151)"
-    assert first_enc[8].strip() == "0.50"                           # VALU busy
+    first_enc = [c.strip() for c in rows[1].split("|")]
+    assert first_enc[2] == "encode" and "k_quant_rows<unsigned short, false, false>" in first_enc[3]
+    assert first_enc[4] == "120.0"                                  # us from the kernel trace
+    assert first_enc[5] == "537 (537)"                               # 2 B/element read, scaled by 0.5
+    assert first_enc[6] == "151 (151)"
+    n = N_SWEEP
+    assert first_enc[7] == f"{(2 * n + n // 2 + n // 16) / 120e-6 / 1e9:.0f}"   # trace time
+    assert first_enc[8] == "0.50"                                    # VALU busy
+    assert first_enc[9] == "110.0"                                   # the counter run's own time
+    assert first_enc[10] == "1.82"                                   # 2e5 cycles in 110 us
     assert "(2.00 and 1.00)" not in md and "(0.50 and 1.00)" in md
 
 
@@ -77,7 +114,8 @@ def test_quant_counter_order_is_checked(tmp_path):
         sw[40], sw[41] = sw[41], sw[40]          # a dispatch out of the expected order
         write_run(str(tmp_path / tag), disp + sw)
     with pytest.raises(SystemExit, match="unexpected dispatch order"):
-        bench.reduce_quant_counters(str(tmp_path / "fetch"), str(tmp_path / "write"), str(tmp_path / "valu"))
+        bench.reduce_quant_counters(str(tmp_path / "fetch"), str(tmp_path / "write"), str(tmp_path / "valu"),
+                                    str(tmp_path / "valu"))
 
 
 def test_gemm_launches():
@@ -124,3 +162,37 @@ def test_busy_reduction(tmp_path):
     row = [c.strip() for c in md.splitlines()[-1].split("|")]
     # dispatches, ms, GHz, MFMA busy, VALU/MFMA, VALU active, issue wait, LDS conflict
     assert row[2:10] == ["2", "1.000", "2.00", "0.500", "6.00", "0.500", "0.250", "0.100"]
+
+
+def test_trace_reduction(tmp_path):
+    """GEMM launches classified by kernel and grid, the timed steps' average
+    set against the bench line's events, and the sweep's passes summed."""
+    steps, warmup = 3, 1
+    kinds = dict(bench.gemm_kinds())
+    disp = []
+    for k in range(warmup + steps):
+        for name, us in (("fprop", 200), ("dgrad", 1200), ("wgrad", 1250 + 10 * k)):
+            kern, grid = kinds[name]
+            disp.append((f"void nvfp4::(anonymous namespace)::{kern}(...)", grid, us * 1000))
+    disp += [(n, g, dur) for n, g, dur, _ in sweep_dispatches(lambda kind: {})]
+    stats = [{"Name": "void nvfp4::(anonymous namespace)::k_gemm_nvfp4_sk<false, true>(...)", "Calls": 8,
+              "TotalDurationNs": 8e6, "AverageNs": 1e6, "Percentage": 50.0, "MinNs": 9e5, "MaxNs": 1.1e6,
+              "StdDev": 1.0}]
+    write_trace(str(tmp_path / "t"), disp, stats)
+    sweep = {f"axis{a} {r}{'+rht' if h else ''}": {"ms": 0.21} for a, r, h in bench.SWEEP_VARIANTS}
+    line = {"value": 1000.0, "unit": "TFLOP/s", "ms_per_step": 3.2, "steps": steps, "warmup": warmup,
+            "roofline": {"avg_launch_ms": 1.3, "frac": 0.53}, "breakdown": {"gemm wgrad": {"ms": 1.3}},
+            "quantize_sweep_32768x8192_bf16": sweep}
+    bj = tmp_path / "bench.json"
+    bj.write_text("log line\n" + __import__("json").dumps(line) + "\n")
+    md = bench.reduce_trace(str(tmp_path / "t"), str(bj))
+    wg = [l for l in md.splitlines() if l.startswith("| wgrad")][0].split("|")
+    assert wg[4].strip() == str(warmup + steps)
+    assert [c.strip() for c in wg[5:8]] == ["1.2700", "1.2600", "1.2800"]   # the last 3 launches
+    assert wg[8].strip() == "1.3"                                            # the bench line's events
+    assert f"{1.27:.4f} ms, i.e. frac {2 * 5120 * 20480 * 8192 / 1.27e-3 / 1e12 / 2500:.4f}" in md
+    fp = [l for l in md.splitlines() if l.startswith("| fprop")][0].split("|")
+    assert fp[5].strip() == "0.2000"
+    sw = [l for l in md.splitlines() if l.startswith("| axis1 rne |")][0].split("|")
+    assert [c.strip() for c in sw[2:6]] == ["90.0", "110.0", "202.0", "210.0"]
+    assert "`k_gemm_nvfp4_sk<false, true>`" in md
