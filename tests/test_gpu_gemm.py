@@ -56,6 +56,7 @@ def _check(c_gpu, ref_a, ref_b, out, rows=None, cols=None, label=""):
         c_gpu = c_gpu[:, torch.as_tensor(cols)]
     if out == "f32":
         ok, worst = oracle.check_gemm_f32(c_gpu.double().numpy(), cref, bound, RTOL)
+        print(f"[gemm] {label}: worst |err|/bound = {worst:.3e}", flush=True)
         assert ok, f"{label}: worst |err|/bound = {worst:.3e} > {RTOL}"
         return worst
     ok, nbad = oracle.check_gemm_bf16(c_gpu.double().numpy(), cref, bound, RTOL)

@@ -21,6 +21,7 @@ def _ref(qa, qb):
 
 def _close_f32(got, c, bound, label):
     ok, worst = oracle.check_gemm_f32(got, c, bound, 1e-5)
+    print(f"[linear] {label}: worst |err|/bound = {worst:.3e}", flush=True)
     assert ok, f"{label}: worst |err|/bound = {worst:.3e}"
 
 

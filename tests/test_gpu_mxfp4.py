@@ -53,6 +53,7 @@ def _gemm_case(m, n, k, out, seed=1):
     cref, bound = oracle.mxfp4_gemm(ra, rb)
     if out == "f32":
         ok, worst = oracle.check_gemm_f32(c.cpu().numpy(), cref, bound, 1e-5)
+        print(f"[mxfp4 gemm] {m}x{n}x{k}: worst |err|/bound = {worst:.3e}", flush=True)
         assert ok, f"{m}x{n}x{k}: worst |err|/bound = {worst:.3e}"
     else:
         ok, nbad = oracle.check_gemm_bf16(c.double().cpu().numpy(), cref, bound, 1e-5)
@@ -108,6 +109,7 @@ def test_full_workload_step(name):
     got = c[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")].double().cpu().numpy()
     if g.out == "f32":
         ok, worst = oracle.check_gemm_f32(got, cref, bound, 1e-5)
+        print(f"[mxfp4 gemm] {name}: worst |err|/bound = {worst:.3e}", flush=True)
         assert ok, f"{name}: worst |err|/bound = {worst:.3e}"
     else:
         ok, nbad = oracle.check_gemm_bf16(got, cref, bound, 1e-5)
