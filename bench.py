@@ -12,7 +12,10 @@ resident in HBM before timing starts:
 dY's two quantizations run as one dual-layout call (one amax read for both);
 W's axis-0 and X's axis-0 RHT quantizations (the backward operands of
 forward-time tensors) run on a second stream beside the fprop GEMM.
-value = GEMM FLOP of the step / step time (quantization included), TFLOP/s.
+value = GEMM FLOP of the step / step time (quantization included), TFLOP/s,
+timed over K steps that record events only at each step's start and around
+the wgrad launch; the per-op breakdown comes from K more steps with an event
+after every op.
 Also reported: quantizer GB/s per operand and on the 32768x8192 sweep tensor
 (RNE/SR x RHT off/on) and its dequantize to bf16 and f32, the fprop operands'
 quantization warm and after a 512 MiB cache flush, per-GEMM TFLOP/s, the
@@ -260,28 +263,36 @@ def reduce_trace(trace_dir: str, bench_json: str) -> str:
            f"({steps} timed steps after {warmup} warm-up; the tracer slows the step).", ""]
     # GEMM launches
     out += ["## GEMM launches", "",
-            "Each layer GEMM is one `nvfp4_gemm_ws` launch, identified by kernel and grid size. The last "
-            f"{steps} launches of each are the timed steps'.", "",
-            "| GEMM | kernel | work-items | launches | trace avg of timed ms | min | max | bench events ms | "
-            "TFLOP/s (trace) | of 2.5 PF/s |", "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+            "Each layer GEMM is one `nvfp4_gemm_ws` launch, identified by kernel and grid size. The bench runs "
+            f"{warmup} warm-up steps, {steps} timed steps (events only at the step start and around the wgrad "
+            f"launch) and {steps} breakdown steps (an event after every op); the columns below average the "
+            "timed steps' launches and, separately, the breakdown steps'.", "",
+            "| GEMM | kernel | work-items | launches | trace avg of timed ms | min | max | "
+            "trace avg of breakdown ms | bench events ms | TFLOP/s (trace, timed) | of 2.5 PF/s |",
+            "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
     import workloads
     gemms = {"fprop": workloads.FPROP, "dgrad": workloads.DGRAD, "wgrad": workloads.WGRAD}
     bd = b.get("breakdown", {})
+    rf = b.get("roofline", {})
     dom = None
     for name, (kern, grid) in gemm_kinds():
         launches = [(e[3] - e[2]) / 1e6 for e in ds if kern in e[0] and e[1] == grid]
-        if len(launches) < steps:
-            raise SystemExit(f"--trace: {len(launches)} launches of {kern} ({grid}) < {steps} steps")
-        t = launches[-steps:]
+        if len(launches) != warmup + 2 * steps:
+            raise SystemExit(f"--trace: {len(launches)} launches of {kern} ({grid}), expected "
+                             f"{warmup} + 2 x {steps}")
+        t = launches[warmup:warmup + steps]
+        t_bd = launches[warmup + steps:]
         avg = sum(t) / len(t)
         tf = gemms[name].flops / (avg * 1e-3) / 1e12
-        ev = bd.get("gemm " + name, {}).get("ms")
+        # the timed pass has events around wgrad only; the others' come from the breakdown pass
+        ev = rf.get("avg_launch_ms") if name == "wgrad" else bd.get("gemm " + name, {}).get("ms")
         out.append(f"| {name} | `{kern}` | {grid} | {len(launches)} | {avg:.4f} | {min(t):.4f} | {max(t):.4f} | "
-                   f"{ev} | {tf:.1f} | {tf / PEAK_F16_TFLOPS:.4f} |")
+                   f"{sum(t_bd) / len(t_bd):.4f} | {ev} | {tf:.1f} | {tf / PEAK_F16_TFLOPS:.4f} |")
         if name == "wgrad":
             dom = (avg, tf)
-    rf = b.get("roofline", {})
-    out += ["", f"Dominant kernel (wgrad's launch): the bench line reports `avg_launch_ms` {rf.get('avg_launch_ms')} "
+    out += ["", "bench events: wgrad's from the timed steps' events around it, fprop's and dgrad's from the "
+            "breakdown steps.", "",
+            f"Dominant kernel (wgrad's launch): the bench line reports `avg_launch_ms` {rf.get('avg_launch_ms')} "
             f"and `frac` {rf.get('frac')} from its HIP events; the trace average of the same {steps} launches is "
             f"{dom[0]:.4f} ms, i.e. frac {dom[1] / PEAK_F16_TFLOPS:.4f}.", ""]
     # quantizer sweep
@@ -519,6 +530,13 @@ def main():
     torch.cuda.set_device(0)
     nv.lib()
     dev = torch.device("cuda", 0)
+
+    def hold_gpu():
+        # Event-timed regions that start on an idle GPU: a spin kernel of
+        # about 0.2 ms (500k core clocks) queued ahead of the start event, so
+        # the host's launch of the first timed call happens while the GPU is
+        # still busy and its latency stays out of the measured interval.
+        torch.cuda._sleep(500_000)
     mask = workloads.rht_sign_mask()
     seed = workloads.SR_SEED
 
@@ -541,6 +559,7 @@ def main():
     copy_ms = []
     for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_gpu()
         e0.record()
         calib_dst.copy_(calib_src)
         e1.record()
@@ -595,11 +614,17 @@ def main():
     release_after = next(i for i, (n, _, _) in enumerate(ops) if n == "q fprop W")
     first_wait = next(i for i, (n, _, _) in enumerate(ops) if n == "gemm dgrad")
 
-    def step(start_ev, release_ev, side_done, events=None):
-        start_ev.record(main_stream)
+    def step(start_ev, release_ev, side_done, events=None, wgrad_evs=None):
+        """One step.  `events`: an event after every op (the breakdown pass);
+        `wgrad_evs`: a pair of events around the wgrad launch only (the timed
+        pass, which records nothing else)."""
+        if start_ev is not None:
+            start_ev.record(main_stream)
         for i in main_ix:
             if i == first_wait:
                 main_stream.wait_event(side_done)
+            if wgrad_evs is not None and i == wgrad_ix:
+                wgrad_evs[0].record(main_stream)
             ops[i][1]()
             if events is not None:
                 events[i].record(main_stream)
@@ -612,35 +637,53 @@ def main():
                         if events is not None:
                             events[j].record(side_stream)
                 side_done.record(side_stream)
+        if wgrad_evs is not None:
+            wgrad_evs[1].record(main_stream)
 
+    wgrad_ix = next(i for i, (n, _, _) in enumerate(ops) if n == "gemm wgrad")
+    assert wgrad_ix == main_ix[-1]
     K = args.steps
     nev = max(K, args.warmup)
     start = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-    release = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    release = [torch.cuda.Event() for _ in range(nev)]
     side_done = [torch.cuda.Event() for _ in range(nev)]
     for w in range(args.warmup):
-        step(start[w], release[w], side_done[w])
+        step(None, release[w], side_done[w])
     torch.cuda.synchronize()
 
     # ---------------------------------------------------- timed region ----
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in ops] for _ in range(K)]
+    # Inside it only three events per step: the step start and the two
+    # around the wgrad launch (an event after every op costs about 1 % of
+    # the step).
+    wg_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for s in range(K):
-        step(start[s], release[s], side_done[s], evs[s])
+        step(start[s], release[s], side_done[s], wgrad_evs=wg_evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    wgrad_ms = np.array([a.elapsed_time(b) for a, b in wg_evs])
+    step_ms = np.array([start[s].elapsed_time(wg_evs[s][1]) for s in range(K)])
+
+    # ------------------------------------------------ breakdown pass ----
+    # K more steps with an event after every op, for the per-op times (not
+    # the headline: the events themselves slow the step)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in ops] for _ in range(K)]
+    rel_t = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_bd = time.perf_counter()
+    for s in range(K):
+        step(start[s], rel_t[s], side_done[s], evs[s])
+    torch.cuda.synchronize()
+    bd_ms_per_step = (time.perf_counter() - t_bd) * 1e3 / K
     per_op = np.zeros((K, len(ops)))
-    step_ms = np.zeros(K)
     for s in range(K):
         # each stream's ops timed back to back: the main stream's from the
         # step start, the second stream's from its release
-        for ix, t0 in ((main_ix, start[s]), (side_ix, release[s])):
+        for ix, t0 in ((main_ix, start[s]), (side_ix, rel_t[s])):
             prev = t0
             for i in ix:
                 per_op[s, i] = prev.elapsed_time(evs[s][i])
                 prev = evs[s][i]
-        step_ms[s] = start[s].elapsed_time(evs[s][main_ix[-1]])
     ms_per_step = wall * 1e3 / K
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -663,10 +706,9 @@ def main():
     # dominant kernel: the one kernel launch with the most time per step,
     # wgrad's (2*5120*20480*8192 flop; f32-output stream-K kernel, as dgrad's
     # but on a larger grid; fprop's is the bf16 one); one GEMM call is one
-    # kernel launch on torch's current stream, which the events above are
-    # recorded on
-    gi = [i for i, (n, _, _) in enumerate(ops) if n == "gemm wgrad"]
-    g_ms = float(np.mean(per_op[:, gi]))
+    # kernel launch on torch's current stream, which the two events of the
+    # timed region around it are recorded on
+    g_ms = float(np.mean(wgrad_ms))
     g_flop = Wg.flops
     achieved = g_flop / (g_ms * 1e-3) / 1e12
     traffic = load_traffic()
@@ -705,6 +747,7 @@ def main():
                     n_it = 10
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     torch.cuda.synchronize()
+                    hold_gpu()
                     e0.record()
                     for _ in range(n_it):
                         call()
@@ -751,6 +794,7 @@ def main():
                 nv.nvfp4_dequantize(qT, dt, out=yq)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
+            hold_gpu()
             e0.record()
             for _ in range(10):
                 nv.nvfp4_dequantize(qT, dt, out=yq)
@@ -780,6 +824,7 @@ def main():
                                     ("cold", lambda: flush.fill_(1))):
                     prep()
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    hold_gpu()
                     e0.record()
                     nv.nvfp4_quantize(x, axis=1, out=out)
                     e1.record()
@@ -809,6 +854,7 @@ def main():
             times = []
             for _ in range(5):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                hold_gpu()
                 e0.record()
                 fn()
                 e1.record()
@@ -946,6 +992,7 @@ def main():
         "pages_context": PAGES_CONTEXT,
         "device": torch.cuda.get_device_name(0),
         "step_ms_event_median": round(float(np.median(step_ms)), 4),
+        "breakdown_pass_ms_per_step": round(bd_ms_per_step, 4),
     }
     print(json.dumps(rec), flush=True)
 

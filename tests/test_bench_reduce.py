@@ -170,7 +170,7 @@ def test_trace_reduction(tmp_path):
     steps, warmup = 3, 1
     kinds = dict(bench.gemm_kinds())
     disp = []
-    for k in range(warmup + steps):
+    for k in range(warmup + 2 * steps):      # warm-up, timed and breakdown steps
         for name, us in (("fprop", 200), ("dgrad", 1200), ("wgrad", 1250 + 10 * k)):
             kern, grid = kinds[name]
             disp.append((f"void nvfp4::(anonymous namespace)::{kern}(...)", grid, us * 1000))
@@ -181,18 +181,20 @@ def test_trace_reduction(tmp_path):
     write_trace(str(tmp_path / "t"), disp, stats)
     sweep = {f"axis{a} {r}{'+rht' if h else ''}": {"ms": 0.21} for a, r, h in bench.SWEEP_VARIANTS}
     line = {"value": 1000.0, "unit": "TFLOP/s", "ms_per_step": 3.2, "steps": steps, "warmup": warmup,
-            "roofline": {"avg_launch_ms": 1.3, "frac": 0.53}, "breakdown": {"gemm wgrad": {"ms": 1.3}},
+            "roofline": {"avg_launch_ms": 1.3, "frac": 0.53}, "breakdown": {"gemm fprop": {"ms": 0.21}},
             "quantize_sweep_32768x8192_bf16": sweep}
     bj = tmp_path / "bench.json"
     bj.write_text("log line\n" + __import__("json").dumps(line) + "\n")
     md = bench.reduce_trace(str(tmp_path / "t"), str(bj))
     wg = [l for l in md.splitlines() if l.startswith("| wgrad")][0].split("|")
-    assert wg[4].strip() == str(warmup + steps)
-    assert [c.strip() for c in wg[5:8]] == ["1.2700", "1.2600", "1.2800"]   # the last 3 launches
-    assert wg[8].strip() == "1.3"                                            # the bench line's events
+    assert wg[4].strip() == str(warmup + 2 * steps)
+    assert [c.strip() for c in wg[5:8]] == ["1.2700", "1.2600", "1.2800"]   # the timed steps' launches
+    assert wg[8].strip() == "1.3000"                                         # the breakdown steps'
+    assert wg[9].strip() == "1.3"                                            # the timed pass's events
     assert f"{1.27:.4f} ms, i.e. frac {2 * 5120 * 20480 * 8192 / 1.27e-3 / 1e12 / 2500:.4f}" in md
     fp = [l for l in md.splitlines() if l.startswith("| fprop")][0].split("|")
     assert fp[5].strip() == "0.2000"
+    assert fp[9].strip() == "0.21"                                            # the breakdown pass's events
     sw = [l for l in md.splitlines() if l.startswith("| axis1 rne |")][0].split("|")
     assert [c.strip() for c in sw[2:6]] == ["90.0", "110.0", "202.0", "210.0"]
     assert "`k_gemm_nvfp4_sk<false, true>`" in md
