@@ -176,12 +176,35 @@ __device__ __forceinline__ uint4 sr_words8(uint64_t g, uint64_t seed, uint64_t o
 // stabilizujace ..."): sign flips from the mask, the Walsh-Hadamard
 // butterfly with stages 1, 2, 4, 8 (lower index a+b, upper a-b), then the
 // exact factor 1/4.
-__device__ __forceinline__ void rht16(float *t, uint32_t sign_mask) {
+//
+// The signs as factors +-1, one per element (wave-uniform).
+struct RhtSigns {
+  float s[16];
+};
+__device__ __forceinline__ RhtSigns rht_signs(uint32_t sign_mask) {
+  RhtSigns r;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    t[j] = ((sign_mask >> j) & 1u) ? -t[j] : t[j];
+  for (int j = 0; j < 16; ++j) r.s[j] = ((sign_mask >> j) & 1u) ? -1.0f : 1.0f;
+  return r;
+}
+
+// 4y, the transform without its factor 1/4.  The sign flips ride in the
+// first stage: b = s_{j+1} x_{j+1} is an exact product, and fma(x_j, s_j, +-b)
+// rounds s_j x_j +- b once, as the addition of the flipped values does, so
+// every stage output is bit for bit the one of flip-then-butterfly (one
+// multiply and two fused multiply-adds per pair instead of two flips and
+// two additions).
+__device__ __forceinline__ void rht16_x4(float *t, const RhtSigns &sg) {
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int j = 0; j < 16; j += 2) {
+    const float b = t[j + 1] * sg.s[j + 1];
+    const float a0 = __builtin_fmaf(t[j], sg.s[j], b);
+    const float a1 = __builtin_fmaf(t[j], sg.s[j], -b);
+    t[j] = a0;
+    t[j + 1] = a1;
+  }
+#pragma unroll
+  for (int h = 2; h < 16; h <<= 1) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j & h) continue;
@@ -190,8 +213,19 @@ __device__ __forceinline__ void rht16(float *t, uint32_t sign_mask) {
       t[j + h] = a - b;
     }
   }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) t[j] = 0.25f * t[j];
+}
+
+// The 1/4 of the transform moved out of the values.  amax: the maximum of
+// |4y| taken as a bit pattern, then multiplied by 1/4 once (x -> x/4 is
+// monotone, so this is the bit pattern of max |y| for any input; a NaN stays
+// a NaN).  Encode of bf16 input: 4y is exact (every value the butterfly
+// forms from bf16 inputs is a multiple of 2^-133, so y = (4y)/4 is exact
+// too), so the block maximum times k/4 and the element times m/4 are the
+// same real products as y times k and m, and round the same, as long as
+// k/4 and m/4 are exact: k >= 448/FLT_MAX always is, and every multiplier
+// m >= s_enc/448 is when s_enc >= 2^-115 (amax below about 1.1e38).
+__device__ __forceinline__ uint32_t quarter_bits(uint32_t bits) {
+  return __float_as_uint(0.25f * __uint_as_float(bits));
 }
 
 // Largest |value| of 16 binary32 values as a bit pattern (exact, NaN > Inf).
@@ -235,6 +269,19 @@ __device__ __forceinline__ uint32_t block_scale(uint32_t bmax_bits, const Tensor
 __device__ __forceinline__ void fill_scale_lut(float *lut, const TensorScales &ts, int t0) {
   const int i = (int)threadIdx.x - t0;
   if (i >= 0 && i < 128) lut[i] = (i == 0 || i > 0x7E) ? 0.0f : __fdiv_rn(ts.s_enc, e4m3_to_f32((uint32_t)i));
+}
+
+// The tensor scales for block values taken as 4y (the transform without its
+// 1/4): k/4 and s_enc/4, so block scales and multipliers come out as for y
+// (the multipliers as m/4).  Exact when s_enc >= 2^-115 (quarter_exact):
+// then k/4, s_enc/4 and every s_enc/4 / e4m3(S) >= s_enc / 1792 are normal,
+// and a quotient scaled by a power of two rounds the same.  g is kept.
+__device__ __forceinline__ bool quarter_exact(const TensorScales &ts) { return ts.s_enc >= 0x1p-115f; }
+__device__ __forceinline__ TensorScales quarter_scales(const TensorScales &ts) {
+  TensorScales q = ts;
+  q.k = 0.25f * ts.k;
+  q.s_enc = 0.25f * ts.s_enc;
+  return q;
 }
 
 __device__ __forceinline__ uint32_t block_scale_lut(uint32_t bmax_bits, const TensorScales &ts, const float *lut,

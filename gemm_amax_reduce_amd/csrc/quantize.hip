@@ -181,7 +181,8 @@ __global__ void __launch_bounds__(kQT) k_amax_flat(const uint4 *x, int64_t n16, 
 template <typename T>
 __global__ void __launch_bounds__(kQT) k_amax_rht_rows(const T *x, int64_t nchunks, int64_t per_wg, uint32_t sign_mask,
                                                       uint32_t *amax_bits) {
-  uint32_t m = 0;
+  const RhtSigns sg = rht_signs(sign_mask);
+  uint32_t m = 0;                    // max |4y| (bit pattern)
   const int64_t beg = (int64_t)blockIdx.x * per_wg;
   const int64_t end = beg + per_wg < nchunks ? beg + per_wg : nchunks;
   int64_t c = beg + threadIdx.x;
@@ -189,17 +190,17 @@ __global__ void __launch_bounds__(kQT) k_amax_rht_rows(const T *x, int64_t nchun
     float y0[16], y1[16];
     Load16<T>::run(x + 16 * c, y0);
     Load16<T>::run(x + 16 * (c + kQT), y1);
-    rht16(y0, sign_mask);
-    rht16(y1, sign_mask);
+    rht16_x4(y0, sg);
+    rht16_x4(y1, sg);
     m = max(m, max(absmax_bits16(y0), absmax_bits16(y1)));
   }
   for (; c < end; c += kQT) {
     float y[16];
     Load16<T>::run(x + 16 * c, y);
-    rht16(y, sign_mask);
+    rht16_x4(y, sg);
     m = max(m, absmax_bits16(y));
   }
-  block_max_atomic(m, amax_bits);
+  block_max_atomic(quarter_bits(m), amax_bits);
 }
 
 // ------------------------------------------------------- axis 0 ----
@@ -255,7 +256,8 @@ __global__ void __launch_bounds__(kQT) k_amax_rht_cols(const T *x, int64_t rows,
   const int64_t c = ((int64_t)blockIdx.x * kQT + threadIdx.x) * CPT;
   const int64_t nkb = rows / 16, kb0 = (int64_t)blockIdx.y * kNBT;
   const bool fast = (c + CPT <= cols) && (CPT == 1 || (cols % 2) == 0);
-  uint32_t m = 0;
+  const RhtSigns sg = rht_signs(sign_mask);
+  uint32_t m = 0;                    // max |4y| (bit pattern)
   if (c < cols) {
 #pragma unroll
     for (int i = 0; i < kNBT; ++i) {
@@ -264,12 +266,12 @@ __global__ void __launch_bounds__(kQT) k_amax_rht_cols(const T *x, int64_t rows,
       load_col_block<T>(x, cols, kb0 + i, c, fast, y);
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
-        rht16(y[e], sign_mask);
+        rht16_x4(y[e], sg);
         m = max(m, absmax_bits16(y[e]));
       }
     }
   }
-  block_max_atomic(m, amax_bits);
+  block_max_atomic(quarter_bits(m), amax_bits);
 }
 
 // Dual-layout amax: one read of x gives the plain maximum (for the axis-1
@@ -282,7 +284,8 @@ __global__ void __launch_bounds__(kQT) k_amax_dual_cols(const T *x, int64_t rows
   const int64_t c = ((int64_t)blockIdx.x * kQT + threadIdx.x) * CPT;
   const int64_t nkb = rows / 16, kb0 = (int64_t)blockIdx.y * kNBT;
   const bool fast = (c + CPT <= cols) && (CPT == 1 || (cols % 2) == 0);
-  uint32_t mp = 0, mr = 0;
+  const RhtSigns sg = rht_signs(sign_mask);
+  uint32_t mp = 0, mr = 0;           // max |x|, max |4y| (bit patterns)
   if (c < cols) {
 #pragma unroll
     for (int i = 0; i < kNBT; ++i) {
@@ -292,12 +295,12 @@ __global__ void __launch_bounds__(kQT) k_amax_dual_cols(const T *x, int64_t rows
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
         mp = max(mp, absmax_bits16(y[e]));
-        rht16(y[e], sign_mask);
+        rht16_x4(y[e], sg);
         mr = max(mr, absmax_bits16(y[e]));
       }
     }
   }
-  block_max2_atomic(mp, plain_bits, mr, rht_bits);
+  block_max2_atomic(mp, plain_bits, quarter_bits(mr), rht_bits);
 }
 
 // ------------------------------------------------------------- encode ----
@@ -311,11 +314,16 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
   const float amax = meta[0];
   const TensorScales ts = tensor_scales(amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) meta[1] = ts.g;
+  // with the transform on bf16 input, the blocks are taken as 4y and the
+  // scales as k/4, s_enc/4 where that is exact (see quarter_scales)
+  const bool fold = RHT && sizeof(T) == 2 && quarter_exact(ts);
+  const TensorScales tb = fold ? quarter_scales(ts) : ts;
+  const RhtSigns sg = rht_signs(sign_mask);
   // stochastic rounding walks several blocks per thread: their multipliers
   // come from a per-workgroup table
   __shared__ float lut[128];
   if constexpr (SR) {
-    fill_scale_lut(lut, ts, 0);
+    fill_scale_lut(lut, tb, 0);
     __syncthreads();
   }
   const int64_t stride = (int64_t)gridDim.x * kQT;
@@ -323,9 +331,15 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
     const int64_t b = nblocks - 1 - i;
     float y[16];
     Load16<T>::run(x + 16 * b, y);
-    if (RHT) rht16(y, sign_mask);
+    if (RHT) {
+      rht16_x4(y, sg);
+      if (!fold) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = 0.25f * y[j];
+      }
+    }
     float m;
-    uint32_t S = SR ? block_scale_lut(absmax_bits16(y), ts, lut, &m) : block_scale(absmax_bits16(y), ts, &m);
+    uint32_t S = SR ? block_scale_lut(absmax_bits16(y), tb, lut, &m) : block_scale(absmax_bits16(y), tb, &m);
     store_nt(codes + b, encode16<SR>(y, m, (uint64_t)b, seed, offset));
     store_nt(scales + b, (uint8_t)S);
   }
@@ -347,8 +361,13 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
   // before it is written back (pieces from different workgroups, possibly on
   // different XCDs, left L2 as partial lines: +25-45 % HBM write bytes).
   static_assert(kQT == 256, "four waves per workgroup");
+  // with the transform on bf16 input, the blocks are taken as 4y and the
+  // scales as k/4, s_enc/4 where that is exact (see quarter_scales)
+  const bool fold = RHT && sizeof(T) == 2 && quarter_exact(ts);
+  const TensorScales tb = fold ? quarter_scales(ts) : ts;
+  const RhtSigns sg = rht_signs(sign_mask);
   __shared__ float lut[128];         // multipliers of the block scale codes
-  fill_scale_lut(lut, ts, 0);
+  fill_scale_lut(lut, tb, 0);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c = ((int64_t)(gridDim.x - 1 - blockIdx.x) * 64 + lane) * CPT;
@@ -365,9 +384,15 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
     load_col_block<T>(x, cols, kb0 + i, c, fast, y);
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-      if (RHT) rht16(y[e], sign_mask);
+      if (RHT) {
+        rht16_x4(y[e], sg);
+        if (!fold) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) y[e][j] = 0.25f * y[e][j];
+        }
+      }
       float m;
-      const uint32_t S = block_scale_lut(absmax_bits16(y[e]), ts, lut, &m);
+      const uint32_t S = block_scale_lut(absmax_bits16(y[e]), tb, lut, &m);
       const int64_t blk = (c + e) * nkb + kb0 + i;   // block index in the [outer][K/16] layout
       cw[e][i] = encode16<SR>(y[e], m, (uint64_t)blk, seed, offset);
       sc[e] |= S << (8 * i);
@@ -514,11 +539,16 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
     meta1[1] = ts1.g;
     meta0[1] = ts0.g;
   }
+  // axis 0 with the transform on bf16 input: blocks taken as 4y, scales as
+  // k/4, s_enc/4 where that is exact (see quarter_scales)
+  const bool fold0 = RHT0 && sizeof(T) == 2 && quarter_exact(ts0);
+  const TensorScales tb0 = fold0 ? quarter_scales(ts0) : ts0;
+  const RhtSigns sg0 = rht_signs(sign_mask0);
   // multipliers of the block scale codes of each layout (the staging
   // barrier below orders these writes before their reads)
   __shared__ float lut1[128], lut0[128];
   fill_scale_lut(lut1, ts1, 0);
-  fill_scale_lut(lut0, ts0, 128);
+  fill_scale_lut(lut0, tb0, 128);
   // ---- stage the tile (rows past `rows` and chunks past `cols` skipped:
   // no block that reads them is encoded)
   constexpr int kChunksRow = kDualCols / E;
@@ -584,9 +614,15 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
       float y[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(*reinterpret_cast<const T *>(tile + (16 * i + j) * kPitch + t * (int)sizeof(T)));
-      if (RHT0) rht16(y, sign_mask0);
+      if (RHT0) {
+        rht16_x4(y, sg0);
+        if (!fold0) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) y[j] = 0.25f * y[j];
+        }
+      }
       float m;
-      const uint32_t S = block_scale_lut(absmax_bits16(y), ts0, lut0, &m);
+      const uint32_t S = block_scale_lut(absmax_bits16(y), tb0, lut0, &m);
       cw[i] = encode16<SR0>(y, m, (uint64_t)(gc * nb0 + gr / 16), seed0, offset0);
       sc |= S << (8 * i);
       nvalid = i + 1;
