@@ -703,7 +703,12 @@ dim3 col_tiles(int64_t rows, int64_t cols, bool bf16) {
 void launch_amax_flat(const void *x, bool bf16, int64_t n, uint32_t *amax_bits, uint32_t *amax_bits2,
                       hipStream_t stream) {
   const int64_t n16 = n * (bf16 ? 2 : 4) / 16;
-  const unsigned g = grid_for(n16, kQT * 4, 1024);
+  // 1024 workgroups, or 512 where a thread would have fewer than 16
+  // vectors (tensors below 64 MiB): there the workgroups finish together
+  // and their atomics queue on one address.  Measured on MI355X: the 40-50
+  // MB layer operands quantize 3-7 us faster with 512, the 512 MiB sweep
+  // tensor 5-8 us slower.
+  const unsigned g = grid_for(n16, kQT * 4, n16 < (int64_t)kQT * 16 * 1024 ? 512 : 1024);
   const int64_t per = (n16 + g - 1) / g;
   if (bf16) hipLaunchKernelGGL(k_amax_flat<uint16_t>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits, amax_bits2);
   else hipLaunchKernelGGL(k_amax_flat<float>, dim3(g), dim3(kQT), 0, stream, (const uint4 *)x, n16, per, amax_bits, amax_bits2);

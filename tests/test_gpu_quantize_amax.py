@@ -56,3 +56,36 @@ def test_amax_empty_is_zero():
     a = nv.nvfp4_amax(torch.empty(0, 32, device="cuda"))
     torch.cuda.synchronize()
     assert float(a.cpu()[0]) == 0.0
+
+
+@pytest.mark.parametrize("axis,rounding", [(1, "rne"), (1, "sr"), (0, "rne"), (0, "sr")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rht_values_near_the_top_of_the_range(axis, rounding, dtype):
+    """The transform on values near 1e37 (its sums stay finite), quantized
+    with the computed amax and with a supplied 3e38.  With 3e38 the tensor
+    scale s_enc is below 2^-115, where a bf16 encode stops taking the block
+    as 4y with the scales quartered and multiplies the values by 1/4 itself:
+    both forms bit-exact against the oracle."""
+    print(f"[amax] near-top axis={axis} {rounding} {dtype}", flush=True)
+    nv = _nv()
+    x = workloads.mixed_rows(64, 160, 43)
+    x = x / np.abs(x).max() * 1e37
+    xt = torch.from_numpy(x.astype(np.float32)) if dtype == "f32" else workloads.to_bf16(x)
+    xd = xt.cuda()
+    code = oracle.SR if rounding == "sr" else oracle.RNE
+    q = nv.nvfp4_rht_quantize(xd, MASK, axis=axis, rounding=rounding, seed=5, offset=3)
+    torch.cuda.synchronize()
+    r = oracle.quantize(xt, axis=axis, rounding=code, seed=5, offset=3, rht=True, sign_mask=MASK)
+    assert np.isfinite(r.meta).all() and r.meta[0] > 1e36
+    np.testing.assert_array_equal(q.meta.cpu().numpy().view(np.uint32), r.meta.view(np.uint32))
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), r.scales)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), r.codes)
+    amax = torch.tensor([3e38], dtype=torch.float32, device="cuda")
+    q = nv.nvfp4_quantize_amax(xd, amax, axis=axis, rounding=rounding, seed=5, offset=3, rht=True, sign_mask=MASK)
+    torch.cuda.synchronize()
+    r = oracle.quantize(xt, axis=axis, rounding=code, seed=5, offset=3, rht=True, sign_mask=MASK,
+                        amax=float(amax.cpu()[0]))
+    assert r.scales.any()
+    np.testing.assert_array_equal(q.meta.cpu().numpy().view(np.uint32), r.meta.view(np.uint32))
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), r.scales)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), r.codes)
