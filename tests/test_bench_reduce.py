@@ -62,7 +62,9 @@ def sweep_dispatches(counters_of):
         amax = ("k_amax_rht_" + ("rows" if axis else "cols")) if rht else "k_amax_flat"
         enc = "k_quant_%s<unsigned short, %s, %s>" % ("rows" if axis else "cols", str(rnd == "sr").lower(),
                                                       str(rht).lower())
-        for _ in range(bench.SWEEP_CALLS):
+        for c in range(bench.SWEEP_CALLS):
+            if c == 2:       # the spin kernel queued ahead of the timed calls
+                out.append(("at::cuda::(anonymous namespace)::spin_kernel(long)", 1, 200000, counters_of("spin")))
             out.append(("nvfp4::k_meta_init(float*)", 64, 2000, counters_of("meta")))
             out.append((f"void nvfp4::{amax}<unsigned short>(...)", 262144, 90000, counters_of("amax")))
             out.append((f"void nvfp4::{enc}(...)", N_SWEEP // 16, 110000, counters_of("enc")))
@@ -73,8 +75,8 @@ def test_quant_counter_table(tmp_path):
     # the copy reads 2x and writes 1x its size in KiB, so the scales are 0.5 and 1
     kib = bench.CALIB_BYTES / 1024
     step = [("void nvfp4::k_quant_rows<unsigned short, false, false>(...)", 4096 * 5120 // 16, 30000, {})]
-    fetch = {"meta": 0.0, "amax": 2 * 2 * N_SWEEP / 1024, "enc": 2 * 2 * N_SWEEP / 1024}
-    write = {"meta": 0.0, "amax": 0.0, "enc": (N_SWEEP // 2 + N_SWEEP // 16) / 1024}
+    fetch = {"meta": 0.0, "spin": 0.0, "amax": 2 * 2 * N_SWEEP / 1024, "enc": 2 * 2 * N_SWEEP / 1024}
+    write = {"meta": 0.0, "spin": 0.0, "amax": 0.0, "enc": (N_SWEEP // 2 + N_SWEEP // 16) / 1024}
     for tag, cname, per, copyv in (("fetch", "FETCH_SIZE", fetch, 2 * kib), ("write", "WRITE_SIZE", write, kib)):
         disp = [(COPY, 1, 100000, {cname: copyv})]
         disp += [(n, g, dur, {cname: 1.0}) for n, g, dur, _ in step]
