@@ -13,16 +13,22 @@ stochastic rounding of the gradients).
     backward dx = dy W     A = dy (axis 1, SR),  B = W (axis 0, RNE)
              dW = dy^T x   A = dy (axis 0, RHT, SR), B = x (axis 0, RHT, RNE)
 
-dy's two quantizations come from one dual-layout call.  The two operands of
-the weight gradient share one sign mask, so the transform cancels in the
-product.  Every quantization and GEMM runs in the HIP library; there is no
-CPU path.
+Each operand is read once for both of its layouts: x and W through
+dual-layout calls in the forward pass (when their gradients are needed), dy
+in the backward pass.  The backward keeps only the quantized operands, not x
+and W.  The two operands of the weight gradient share one sign mask, so the
+transform cancels in the product.  Every quantization and GEMM runs in the
+HIP library; there is no CPU path.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (nvfp4_gemm_ws, nvfp4_quantize, nvfp4_quantize_dual, nvfp4_rht_quantize, NVFP4Error)
+from . import (nvfp4_gemm_ws, nvfp4_quantize, nvfp4_quantize_dual, NVFP4Error)
+
+
+def _out_dtype(t: torch.Tensor) -> torch.dtype:
+    return torch.bfloat16 if t.dtype == torch.bfloat16 else torch.float32
 
 
 class NVFP4LinearFunction(torch.autograd.Function):
@@ -34,18 +40,29 @@ class NVFP4LinearFunction(torch.autograd.Function):
             raise NVFP4Error("x must be [tokens, in] and weight [out, in]")
         x = x.contiguous()
         weight = weight.contiguous()
-        qx = nvfp4_quantize(x, axis=1)
-        qw = nvfp4_quantize(weight, axis=1)
-        out_dtype = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
-        y = nvfp4_gemm_ws(qx, qw, out_dtype)
-        ctx.save_for_backward(x, weight)
+        need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        # x along its rows for y and, transformed, along its columns for dW;
+        # W along its rows for y and along its columns for dx
+        qx0 = qw0 = None
+        if need_dw:
+            qx, qx0 = nvfp4_quantize_dual(x, rht0=True, sign_mask0=sign_mask)
+        else:
+            qx = nvfp4_quantize(x, axis=1)
+        if need_dx:
+            qw, qw0 = nvfp4_quantize_dual(weight)
+        else:
+            qw = nvfp4_quantize(weight, axis=1)
+        y = nvfp4_gemm_ws(qx, qw, _out_dtype(x))
+        if y.dtype != x.dtype:
+            y = y.to(x.dtype)
+        ctx.qx0, ctx.qw0 = qx0, qw0
+        ctx.x_dtype, ctx.w_dtype = x.dtype, weight.dtype
         ctx.seed, ctx.offset, ctx.sign_mask = seed, offset, sign_mask
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x, weight = ctx.saved_tensors
-        dy = dy.contiguous().to(x.dtype)
+        dy = dy.contiguous().to(ctx.x_dtype)
         # dy along its columns (data gradient) and, transformed, along its
         # rows (weight gradient); distinct Philox offsets keep the two draws
         # independent
@@ -54,11 +71,14 @@ class NVFP4LinearFunction(torch.autograd.Function):
                                          offset0=2 * ctx.offset + 1)
         dx = dw = None
         if ctx.needs_input_grad[0]:
-            qw0 = nvfp4_quantize(weight, axis=0)
-            dx = nvfp4_gemm_ws(qdy1, qw0, torch.float32).to(x.dtype)
+            dx = nvfp4_gemm_ws(qdy1, ctx.qw0, _out_dtype(dy))
+            if dx.dtype != ctx.x_dtype:
+                dx = dx.to(ctx.x_dtype)
         if ctx.needs_input_grad[1]:
-            qx0 = nvfp4_rht_quantize(x, ctx.sign_mask, axis=0)
-            dw = nvfp4_gemm_ws(qdy0, qx0, torch.float32).to(weight.dtype)
+            dw = nvfp4_gemm_ws(qdy0, ctx.qx0, torch.bfloat16 if ctx.w_dtype == torch.bfloat16 else torch.float32)
+            if dw.dtype != ctx.w_dtype:
+                dw = dw.to(ctx.w_dtype)
+        ctx.qx0 = ctx.qw0 = None
         return dx, dw, None, None, None
 
 

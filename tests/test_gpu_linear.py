@@ -148,3 +148,30 @@ def test_full_layer_shape_bf16():
     check(layer.weight.grad, oracle.quantize(dyc, axis=0, rounding=oracle.SR, seed=0x5EED, offset=1, rht=True,
                                              sign_mask=MASK),
           oracle.quantize(xc, axis=0, rht=True, sign_mask=MASK), "dW")
+
+
+def test_gradients_needed_one_at_a_time():
+    """A frozen weight (only dx) or an input without grad (only dW): the
+    forward quantizes each operand in the layouts its gradients need, and
+    the gradient it returns is bit-identical to the one of the layer with
+    both gradients (same weight, seed and step)."""
+    import gemm_amax_reduce_amd.linear as L
+    x0 = torch.from_numpy(workloads.normal(64, 96, 14)).cuda()
+    dy = torch.from_numpy(workloads.laplace(64, 80, 15, 1e-3)).cuda()
+    layers = [L.NVFP4Linear(96, 80, seed=6, sign_mask=MASK, device="cuda", dtype=torch.float32) for _ in range(3)]
+    with torch.no_grad():
+        for la in layers[1:]:
+            la.weight.copy_(layers[0].weight)
+    xa = x0.clone().requires_grad_(True)
+    ya = layers[0](xa)
+    ya.backward(dy)
+    layers[1].weight.requires_grad_(False)
+    xb = x0.clone().requires_grad_(True)
+    yb = layers[1](xb)
+    yb.backward(dy)
+    yc = layers[2](x0.clone())
+    yc.backward(dy)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.detach(), yb.detach()) and torch.equal(ya.detach(), yc.detach())
+    assert torch.equal(xa.grad, xb.grad) and layers[1].weight.grad is None
+    assert torch.equal(layers[0].weight.grad, layers[2].weight.grad)
