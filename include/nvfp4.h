@@ -148,7 +148,8 @@ int nvfp4_rht_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, i
  * *amax must be finite and >= 0 (not checked): with the true maximum the
  * result equals nvfp4_quantize's bit for bit; a smaller value saturates
  * (block scales at 448, codes at 6), so the decoded values are clipped to
- * +-*amax.  Enqueues two kernels.
+ * +-*amax.  Non-finite input values leave the codes and scales unspecified,
+ * as in nvfp4_quantize.  Enqueues two kernels.
  */
 int nvfp4_amax(const void *x, int x_dtype, int64_t rows, int64_t cols, int axis, int rht,
                uint16_t sign_mask, float *amax, void *hip_stream);
