@@ -236,19 +236,20 @@ __device__ __forceinline__ uint32_t absmax_bits16(const float *y) {
   return m;
 }
 
-// The same for 16 values that come out of arithmetic (the transform's
-// butterfly): eight v_max3_f32 with |.| source modifiers, against 16 masks
-// and 8 integer maxima.  Equal to absmax_bits16 whenever no value is NaN
-// (f32 denormals are kept, so subnormals compare exactly); a NaN here comes
-// only from a non-finite input, whose codes and scales are unspecified.
-// Written as asm: the compiler's float maximum would first quiet every
-// operand it cannot prove canonical.
+// The block maximum of an encode, 16 values as a bit pattern: eight
+// v_max3_f32 with |.| source modifiers, against 16 masks and 8 integer
+// maxima.  Equal to absmax_bits16 whenever no value is NaN (f32 denormals
+// are kept, so subnormals compare exactly); a NaN comes only from a
+// non-finite input, whose codes and scales are unspecified.  The tensor
+// amax keeps the integer form, which orders NaN above Inf.  Written as asm:
+// the compiler's float maximum would first quiet every operand it cannot
+// prove canonical (converted bf16 values among them).
 __device__ __forceinline__ float fmax3_abs(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
-__device__ __forceinline__ uint32_t absmax_bits16_arith(const float *y) {
+__device__ __forceinline__ uint32_t block_absmax_bits16(const float *y) {
   float m = fmax3_abs(y[0], y[1], y[2]);
 #pragma unroll
   for (int j = 3; j < 15; j += 2) m = fmax3_abs(m, y[j], y[j + 1]);

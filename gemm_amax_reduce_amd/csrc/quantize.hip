@@ -339,7 +339,7 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
       }
     }
     float m;
-    const uint32_t bmax = RHT ? absmax_bits16_arith(y) : absmax_bits16(y);
+    const uint32_t bmax = block_absmax_bits16(y);
     uint32_t S = SR ? block_scale_lut(bmax, tb, lut, &m) : block_scale(bmax, tb, &m);
     store_nt(codes + b, encode16<SR>(y, m, (uint64_t)b, seed, offset));
     store_nt(scales + b, (uint8_t)S);
@@ -393,7 +393,7 @@ __global__ void __launch_bounds__(kQT) k_quant_cols(const T *x, int64_t rows, in
         }
       }
       float m;
-      const uint32_t S = block_scale_lut(RHT ? absmax_bits16_arith(y[e]) : absmax_bits16(y[e]), tb, lut, &m);
+      const uint32_t S = block_scale_lut(block_absmax_bits16(y[e]), tb, lut, &m);
       const int64_t blk = (c + e) * nkb + kb0 + i;   // block index in the [outer][K/16] layout
       cw[e][i] = encode16<SR>(y[e], m, (uint64_t)blk, seed, offset);
       sc[e] |= S << (8 * i);
@@ -579,7 +579,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
 #pragma unroll
       for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(src[j]);
       float m;
-      const uint32_t S = block_scale_lut(absmax_bits16(y), ts1, lut1, &m);
+      const uint32_t S = block_scale_lut(block_absmax_bits16(y), ts1, lut1, &m);
       cw[i] = encode16<SR1>(y, m, (uint64_t)(gr * nb1 + gc / 16), seed1, offset1);
       sc |= S << (8 * i);
       nvalid = i + 1;
@@ -623,7 +623,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
         }
       }
       float m;
-      const uint32_t S = block_scale_lut(RHT0 ? absmax_bits16_arith(y) : absmax_bits16(y), tb0, lut0, &m);
+      const uint32_t S = block_scale_lut(block_absmax_bits16(y), tb0, lut0, &m);
       cw[i] = encode16<SR0>(y, m, (uint64_t)(gc * nb0 + gr / 16), seed0, offset0);
       sc |= S << (8 * i);
       nvalid = i + 1;
