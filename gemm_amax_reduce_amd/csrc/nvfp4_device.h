@@ -218,10 +218,11 @@ __device__ __forceinline__ void rht16_x4(float *t, const RhtSigns &sg) {
 // The 1/4 of the transform moved out of the values.  amax: the maximum of
 // |4y| taken as a bit pattern, then multiplied by 1/4 once (x -> x/4 is
 // monotone, so this is the bit pattern of max |y| for any input; a NaN stays
-// a NaN).  Encode of bf16 input: a butterfly output t is a multiple of
-// 2^-133 (the bf16 grid), or at least 2^-109 in magnitude where a sum had to
-// be rounded (it then spans more than 24 bits), so y = t/4 is exact and t is
-// exactly 4y; the block maximum times k/4 and the element times m/4 are then
+// a NaN).  Encode of bf16 input: every value the butterfly forms is a
+// multiple of 2^-133 (the bf16 grid): an exact sum of multiples is one, and
+// a sum is rounded only from 2^-109 up, where the f32 grid is coarser.  So
+// y = t/4, a multiple of 2^-135, is exact and t is exactly 4y; the block
+// maximum times k/4 and the element times m/4 are then
 // the same real products as y times k and m, and round the same, as long as
 // k/4 and m/4 are exact: k >= 448/FLT_MAX always is, and every multiplier
 // m >= s_enc/448 is when s_enc >= 2^-115 (amax below about 1.1e38).
