@@ -550,102 +550,112 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
   __shared__ float lut1[128], lut0[128];
   fill_scale_lut(lut1, ts1, 0);
   fill_scale_lut(lut0, tb0, 128);
-  // ---- stage the tile (rows past `rows` and chunks past `cols` skipped:
-  // no block that reads them is encoded)
-  constexpr int kChunksRow = kDualCols / E;
+  // The body for one tile; W: the whole tile lies inside x (the bounds
+  // checks fold away), which every tile but the last row and column of
+  // tiles is.
+  auto encode_tile = [&](auto whole) {
+    constexpr bool W = decltype(whole)::value;
+    // ---- stage the tile (rows past `rows` and chunks past `cols` skipped:
+    // no block that reads them is encoded)
+    constexpr int kChunksRow = kDualCols / E;
 #pragma unroll
-  for (int i = 0; i < kDualRows * kChunksRow / kQT; ++i) {
-    const int q = i * kQT + t, row = q / kChunksRow, ch = q % kChunksRow;
-    const int64_t gr = r0 + row, gc = c0 + (int64_t)ch * E;
-    if (gr < rows && gc < cols)
-      *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 16) =
-          *reinterpret_cast<const uint4 *>(x + gr * cols + gc);
-  }
-  __syncthreads();
-  const int64_t nb1 = cols / 16, nb0 = rows / 16;
-  // ---- axis 1: row t/4, blocks 4*(t%4) .. +3 of the tile
-  {
-    const int row = t >> 2, cb0 = 4 * (t & 3);
-    const int64_t gr = r0 + row;
-    uint2 cw[4];
-    uint32_t sc = 0;
-    int nvalid = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t gc = c0 + 16 * (cb0 + i);
-      if (gr >= rows || gc >= cols) break;
-      float y[16];
-      const T *src = reinterpret_cast<const T *>(tile + row * kPitch) + 16 * (cb0 + i);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(src[j]);
-      float m;
-      const uint32_t S = block_scale_lut(block_absmax_bits16(y), ts1, lut1, &m);
-      cw[i] = encode16<SR1>(y, m, (uint64_t)(gr * nb1 + gc / 16), seed1, offset1);
-      sc |= S << (8 * i);
-      nvalid = i + 1;
+    for (int i = 0; i < kDualRows * kChunksRow / kQT; ++i) {
+      const int q = i * kQT + t, row = q / kChunksRow, ch = q % kChunksRow;
+      const int64_t gr = r0 + row, gc = c0 + (int64_t)ch * E;
+      if (W || (gr < rows && gc < cols))
+        *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 16) =
+            *reinterpret_cast<const uint4 *>(x + gr * cols + gc);
     }
-    const int64_t b = gr * nb1 + (c0 / 16 + cb0);
-    if (nvalid == 4 && aligned_to(codes1 + b, 16)) {
-      uint4 *dst = reinterpret_cast<uint4 *>(codes1 + b);
-      store_nt(dst, make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y));
-      store_nt(dst + 1, make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y));
-    } else {
+    __syncthreads();
+    const int64_t nb1 = cols / 16, nb0 = rows / 16;
+    // ---- axis 1: row t/4, blocks 4*(t%4) .. +3 of the tile
+    {
+      const int row = t >> 2, cb0 = 4 * (t & 3);
+      const int64_t gr = r0 + row;
+      uint2 cw[4];
+      uint32_t sc = 0;
+      int nvalid = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < nvalid) codes1[b + i] = cw[i];
-    }
-    if (nvalid == 4 && aligned_to(scales1 + b, 4)) {
-      store_nt(reinterpret_cast<uint32_t *>(scales1 + b), sc);
-    } else {
+      for (int i = 0; i < 4; ++i) {
+        const int64_t gc = c0 + 16 * (cb0 + i);
+        if (!W && (gr >= rows || gc >= cols)) break;
+        float y[16];
+        const T *src = reinterpret_cast<const T *>(tile + row * kPitch) + 16 * (cb0 + i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < nvalid) scales1[b + i] = (uint8_t)(sc >> (8 * i));
-    }
-  }
-  // ---- axis 0: column t, the tile's four 16-row blocks
-  {
-    const int64_t gc = c0 + t;
-    uint2 cw[4];
-    uint32_t sc = 0;
-    int nvalid = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t gr = r0 + 16 * i;
-      if (gc >= cols || gr >= rows) break;
-      float y[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(*reinterpret_cast<const T *>(tile + (16 * i + j) * kPitch + t * (int)sizeof(T)));
-      if (RHT0) {
-        rht16_x4(y, sg0);
-        if (!fold0) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) y[j] = 0.25f * y[j];
-        }
+        for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(src[j]);
+        float m;
+        const uint32_t S = block_scale_lut(block_absmax_bits16(y), ts1, lut1, &m);
+        cw[i] = encode16<SR1>(y, m, (uint64_t)(gr * nb1 + gc / 16), seed1, offset1);
+        sc |= S << (8 * i);
+        nvalid = i + 1;
       }
-      float m;
-      const uint32_t S = block_scale_lut(block_absmax_bits16(y), tb0, lut0, &m);
-      cw[i] = encode16<SR0>(y, m, (uint64_t)(gc * nb0 + gr / 16), seed0, offset0);
-      sc |= S << (8 * i);
-      nvalid = i + 1;
-    }
-    const int64_t b = gc * nb0 + r0 / 16;
-    if (nvalid == 4 && aligned_to(codes0 + b, 16)) {
-      uint4 *dst = reinterpret_cast<uint4 *>(codes0 + b);
-      dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
-      dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
-    } else {
+      const int64_t b = gr * nb1 + (c0 / 16 + cb0);
+      if ((W || nvalid == 4) && aligned_to(codes1 + b, 16)) {
+        uint4 *dst = reinterpret_cast<uint4 *>(codes1 + b);
+        store_nt(dst, make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y));
+        store_nt(dst + 1, make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y));
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < nvalid) codes0[b + i] = cw[i];
-    }
-    if (nvalid == 4 && aligned_to(scales0 + b, 4)) {
-      *reinterpret_cast<uint32_t *>(scales0 + b) = sc;
-    } else {
+        for (int i = 0; i < 4; ++i)
+          if (i < nvalid) codes1[b + i] = cw[i];
+      }
+      if ((W || nvalid == 4) && aligned_to(scales1 + b, 4)) {
+        store_nt(reinterpret_cast<uint32_t *>(scales1 + b), sc);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < nvalid) scales0[b + i] = (uint8_t)(sc >> (8 * i));
+        for (int i = 0; i < 4; ++i)
+          if (i < nvalid) scales1[b + i] = (uint8_t)(sc >> (8 * i));
+      }
     }
-  }
+    // ---- axis 0: column t, the tile's four 16-row blocks
+    {
+      const int64_t gc = c0 + t;
+      uint2 cw[4];
+      uint32_t sc = 0;
+      int nvalid = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t gr = r0 + 16 * i;
+        if (!W && (gc >= cols || gr >= rows)) break;
+        float y[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = to_f32<T>(*reinterpret_cast<const T *>(tile + (16 * i + j) * kPitch + t * (int)sizeof(T)));
+        if (RHT0) {
+          rht16_x4(y, sg0);
+          if (!fold0) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) y[j] = 0.25f * y[j];
+          }
+        }
+        float m;
+        const uint32_t S = block_scale_lut(block_absmax_bits16(y), tb0, lut0, &m);
+        cw[i] = encode16<SR0>(y, m, (uint64_t)(gc * nb0 + gr / 16), seed0, offset0);
+        sc |= S << (8 * i);
+        nvalid = i + 1;
+      }
+      const int64_t b = gc * nb0 + r0 / 16;
+      if ((W || nvalid == 4) && aligned_to(codes0 + b, 16)) {
+        uint4 *dst = reinterpret_cast<uint4 *>(codes0 + b);
+        dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
+        dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nvalid) codes0[b + i] = cw[i];
+      }
+      if ((W || nvalid == 4) && aligned_to(scales0 + b, 4)) {
+        *reinterpret_cast<uint32_t *>(scales0 + b) = sc;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nvalid) scales0[b + i] = (uint8_t)(sc >> (8 * i));
+      }
+    }
+  };
+  if (r0 + kDualRows <= rows && c0 + kDualCols <= cols)
+    encode_tile(std::true_type{});
+  else
+    encode_tile(std::false_type{});
 }
 
 // ------------------------------------------------------------ launches ----
