@@ -534,8 +534,13 @@ __global__ void __launch_bounds__(kQT) k_dequant_f32(const uint16_t *codes, cons
 // the four row tiles sharing one 128-byte axis-0 output line (256 rows) are
 // consecutive and so run together on one XCD: its L2 then merges their four
 // 32-byte pieces into whole lines before writing them back.  Row tiles run
-// from the end of x back (the amax pass went forwards).
+// from the end of x back (the amax pass went forwards).  The tile height is
+// a parameter (32 or 64 rows); 32-row tiles double the occupancy (LDS-bound
+// at 64: four workgroups per CU) but measured 5 % slower on dY for every
+// rounding setting but both-SR-with-the-transform, where they tie.
 constexpr int kDualRows = 64, kDualCols = 256;
+constexpr int kDualB = kDualRows / 16;     // 16-row blocks per tile column = blocks per thread in each layout
+static_assert(kDualB == 2 || kDualB == 4, "tile height");
 
 template <typename T, bool SR1, bool SR0, bool RHT0>
 __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, int64_t cols, uint64_t seed1,
@@ -548,7 +553,7 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
   const int t = threadIdx.x;
   const int tiles_r = (int)((rows + kDualRows - 1) / kDualRows), tiles_c = (int)((cols + kDualCols - 1) / kDualCols);
   int tr, tc;
-  xcd_tile(blockIdx.x, tiles_r, tiles_c, 4, tr, tc);
+  xcd_tile(blockIdx.x, tiles_r, tiles_c, 256 / kDualRows, tr, tc);
   const int64_t r0 = (int64_t)(tiles_r - 1 - tr) * kDualRows, c0 = (int64_t)tc * kDualCols;
   const TensorScales ts1 = tensor_scales(meta1[0]), ts0 = tensor_scales(meta0[0]);
   if (blockIdx.x == 0 && t == 0) {
@@ -583,15 +588,16 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
     }
     __syncthreads();
     const int64_t nb1 = cols / 16, nb0 = rows / 16;
-    // ---- axis 1: row t/4, blocks 4*(t%4) .. +3 of the tile
+    // ---- axis 1: row t / (16 / kDualB), blocks kDualB * (t % (16 / kDualB)) .. of the tile
     {
-      const int row = t >> 2, cb0 = 4 * (t & 3);
+      constexpr int kTpr = 16 / kDualB;    // threads per tile row
+      const int row = t / kTpr, cb0 = kDualB * (t % kTpr);
       const int64_t gr = r0 + row;
-      uint2 cw[4];
+      uint2 cw[kDualB];
       uint32_t sc = 0;
       int nvalid = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kDualB; ++i) {
         const int64_t gc = c0 + 16 * (cb0 + i);
         if (!W && (gr >= rows || gc >= cols)) break;
         float y[16];
@@ -605,31 +611,35 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
         nvalid = i + 1;
       }
       const int64_t b = gr * nb1 + (c0 / 16 + cb0);
-      if ((W || nvalid == 4) && aligned_to(codes1 + b, 16)) {
+      if ((W || nvalid == kDualB) && aligned_to(codes1 + b, 16)) {
         uint4 *dst = reinterpret_cast<uint4 *>(codes1 + b);
-        store_nt(dst, make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y));
-        store_nt(dst + 1, make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y));
+#pragma unroll
+        for (int h = 0; h < kDualB / 2; ++h)
+          store_nt(dst + h, make_uint4(cw[2 * h].x, cw[2 * h].y, cw[2 * h + 1].x, cw[2 * h + 1].y));
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kDualB; ++i)
           if (i < nvalid) codes1[b + i] = cw[i];
       }
-      if ((W || nvalid == 4) && aligned_to(scales1 + b, 4)) {
-        store_nt(reinterpret_cast<uint32_t *>(scales1 + b), sc);
+      if ((W || nvalid == kDualB) && aligned_to(scales1 + b, kDualB)) {
+        if constexpr (kDualB == 4)
+          store_nt(reinterpret_cast<uint32_t *>(scales1 + b), sc);
+        else
+          __builtin_nontemporal_store((uint16_t)sc, reinterpret_cast<uint16_t *>(scales1 + b));
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kDualB; ++i)
           if (i < nvalid) scales1[b + i] = (uint8_t)(sc >> (8 * i));
       }
     }
-    // ---- axis 0: column t, the tile's four 16-row blocks
+    // ---- axis 0: column t, the tile's kDualB 16-row blocks
     {
       const int64_t gc = c0 + t;
-      uint2 cw[4];
+      uint2 cw[kDualB];
       uint32_t sc = 0;
       int nvalid = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kDualB; ++i) {
         const int64_t gr = r0 + 16 * i;
         if (!W && (gc >= cols || gr >= rows)) break;
         float y[16];
@@ -649,20 +659,24 @@ __global__ void __launch_bounds__(kQT) k_quant_dual(const T *x, int64_t rows, in
         nvalid = i + 1;
       }
       const int64_t b = gc * nb0 + r0 / 16;
-      if ((W || nvalid == 4) && aligned_to(codes0 + b, 16)) {
+      if ((W || nvalid == kDualB) && aligned_to(codes0 + b, 16)) {
         uint4 *dst = reinterpret_cast<uint4 *>(codes0 + b);
-        dst[0] = make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
-        dst[1] = make_uint4(cw[2].x, cw[2].y, cw[3].x, cw[3].y);
+#pragma unroll
+        for (int h = 0; h < kDualB / 2; ++h)
+          dst[h] = make_uint4(cw[2 * h].x, cw[2 * h].y, cw[2 * h + 1].x, cw[2 * h + 1].y);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kDualB; ++i)
           if (i < nvalid) codes0[b + i] = cw[i];
       }
-      if ((W || nvalid == 4) && aligned_to(scales0 + b, 4)) {
-        *reinterpret_cast<uint32_t *>(scales0 + b) = sc;
+      if ((W || nvalid == kDualB) && aligned_to(scales0 + b, kDualB)) {
+        if constexpr (kDualB == 4)
+          *reinterpret_cast<uint32_t *>(scales0 + b) = sc;
+        else
+          *reinterpret_cast<uint16_t *>(scales0 + b) = (uint16_t)sc;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kDualB; ++i)
           if (i < nvalid) scales0[b + i] = (uint8_t)(sc >> (8 * i));
       }
     }
