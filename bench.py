@@ -671,9 +671,10 @@ def main():
     qX2 = nv.NVFP4Tensor.empty(5120, 8192)
     qdYt = nv.NVFP4Tensor.empty(20480, 8192)
     Y = torch.empty((4096, 5120), dtype=torch.bfloat16, device=dev)
-    # the GEMMs run through nvfp4_gemm_ws: it cuts the tiles of a partly
-    # filled last round into K ranges where that is faster (dgrad) and runs
-    # the mixed-width grid of nvfp4_gemm otherwise (fprop, wgrad)
+    # the GEMMs run through nvfp4_gemm_ws: with its workspace the last one to
+    # two rounds of 256 x 256 tiles run as a stream-K tail (the fprop, dgrad
+    # and wgrad layers are 1.25, 2.5 and 6.25 rounds), where nvfp4_gemm runs
+    # its mixed-width grid
     ws = nv.gemm_workspace(dev)
     dX = torch.empty((8192, 5120), dtype=torch.float32, device=dev)
     dW = torch.empty((5120, 20480), dtype=torch.float32, device=dev)
