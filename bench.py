@@ -517,7 +517,7 @@ def main():
         print(md)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU (the path has no multi-GPU code); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
