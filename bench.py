@@ -580,7 +580,7 @@ def main():
     # The sweep follows the MFMA probe with no idle gap (its input is
     # generated and uploaded with the others): after an idle second the chip
     # needs 10-20 ms of load before the VALU-heavy encodes run at full clock
-    # (SR axis 1 on one box: 229 us right after idle, 206 after the probe),
+    # (SR axis 1 on one MI355X: 229 us right after idle, 206 after the probe),
     # and the step's warm-up follows the sweep the same way.
     sweep = None
     dequant = None
@@ -698,7 +698,7 @@ def main():
     # for dgrad, X on axis 0 with the transform for wgrad) are quantized on a
     # second stream (default priority), released once the forward
     # quantizations are issued, so they run beside the fprop GEMM; the dgrad
-    # GEMM waits for them.  Same-box A/B of the step: 3.199 ms on one stream,
+    # GEMM waits for them.  Same-GPU A/B of the step: 3.199 ms on one stream,
     # 3.147 with the second stream released at the step start, 3.122 released
     # after the forward quantizations; outputs bit-identical.
     SIDE = ("q dgrad W (axis0)", "q wgrad X (RHT, axis0)")

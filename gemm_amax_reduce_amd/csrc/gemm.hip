@@ -644,7 +644,7 @@ k_gemm_nvfp4_split(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA
 // two ranges, added in one fixed order, and the last round fills the CUs:
 // the fprop, dgrad and wgrad layers (1.25, 2.5 and 6.25 rounds of work) run
 // it in as many round-times plus two segment starts.  Measured against the
-// mixed 256/128-wide grid on the same box: fprop -9.7 %, dgrad -1.6 % (as
+// mixed 256/128-wide grid on the same GPU: fprop -9.7 %, dgrad -1.6 % (as
 // the split tail), wgrad -0.8 % (that grid's partial last round of 256-wide
 // tiles already overlaps its 128-wide ones).  What keeps the overhead small:
 // the head's flag is raised by the next segment's prologue, whose wait for

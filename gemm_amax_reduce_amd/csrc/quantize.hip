@@ -156,7 +156,7 @@ template <> __device__ __forceinline__ uint32_t vec_absmax<float>(uint4 v) {
 // Input reads of the single-pass-over-the-data loops (the flat amax and
 // the three axis-0 column kernels) carry the nontemporal hint: each input
 // line is read once per pass.  Measured on the 32768 x 8192 bf16 tensor,
-// same box, bit-identical: axis-0 RNE 238.7 -> 214.4 us per quantization,
+// same GPU, bit-identical: axis-0 RNE 238.7 -> 214.4 us per quantization,
 // axis-0 SR 240.6 -> 227.9, the other variants and the dual-layout
 // quantization of dY within the spread.  (The axis-1 encodes read their
 // 32-byte blocks with ordinary loads: the hint on those slowed the variants
@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(kQT) k_quant_rows(const T *x, int64_t nblocks,
 // are visited in reverse order of the amax pass.  Stochastic rounding
 // without the transform is held to five waves per SIMD (85 VGPRs instead of
 // 138 at three): 32768 x 8192 bf16 227.8 -> 219.5 us per quantization on one
-// box, bit-identical; the same bound spills in the other instances.
+// GPU, bit-identical; the same bound spills in the other instances.
 template <bool SR, bool RHT>
 constexpr int kColsMinWaves = SR && !RHT ? 5 : 1;
 
