@@ -128,18 +128,22 @@ __global__ void __launch_bounds__(kQT) k_mx_quant_cols(const T *x, int64_t rows,
 // column remainder), four waves of 128 x BN/2.  K is consumed in groups of
 // 256 (four 64-wide stages); each group's codes (one 128-byte line per row)
 // come into LDS by DMA exactly as in the NVFP4 kernel (chunk c of row R in
-// slot c ^ (R & 7)), its scales (8 bytes per row) by two 4-byte DMAs per 64
-// rows into two planes (plane p: bytes 4p .. 4p+3 of each row).  A stage is
-// one MFMA step: lane (r, h) of fragment f reads chunk 2s'+h of its row (16
-// bytes = one 32-block) and that block's scale byte.  Requires K % 256 == 0.
+// slot c ^ (R & 7)).  The scales of two groups (16 bytes per row, one per
+// 32-block) come in one 16-byte DMA per row, 64 rows per instruction, into
+// one of two pair buffers.  (Per group, two 4-byte DMAs per 64 rows touched
+// one cache line per row and lane: a timing copy without them ran the dgrad
+// shape 15 % faster.)  A stage is one MFMA step: lane (r, h) of fragment f
+// reads chunk 2s'+h of its row (16 bytes = one 32-block) and that block's
+// scale byte.  Requires K % 256 == 0.
 
 constexpr int BM = 256;
 constexpr int kThreads = 256;
 constexpr int kGroupK = 256;
 constexpr int kRowsMax = BM + 256;
 constexpr int kCodeBytes = kRowsMax * 128;      // 64 KB
-constexpr int kScalePlane = kRowsMax * 4;       // 2 KB
-constexpr int kGroupBytes = kCodeBytes + 2 * kScalePlane;
+constexpr int kGroupBytes = kCodeBytes;         // a group buffer: codes only
+constexpr int kScalePair = kRowsMax * 16;       // 8 KB: the scales of two groups
+constexpr int kLdsBytes = 2 * kGroupBytes + 2 * kScalePair;
 constexpr int kGroupM = 8;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -185,14 +189,13 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
       const int lrow = real ? lds_row0 + 8 * qq : spare_row0 + 8 * (qq - 8);
       dma16(dcodes, gbuf + lrow * 128, dv_code, (gin && real) ? 128u * (uint32_t)g + 8u * qq * rb : kOutOfRange);
     }
-    if (part == 2) {   // scales: 2 planes x (128 or 64 rows) per wave
+    if (part == 2 && (g & 1) == 0) {   // scales of groups g, g+1: 128 or 64 rows per wave
+      uint8_t *sbuf = smem + 2 * kGroupBytes + ((g >> 1) & 1) * kScalePair;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int plane = qq & 1, half = qq >> 1;
+      for (int half = 0; half < 2; ++half) {
         const bool real = !(BN == 128 && dma_b && half >= 1);
         const int lrow = real ? lds_row0 + 64 * half : spare_row0;
-        dma4(dscales, gbuf + kCodeBytes + plane * kScalePlane + lrow * 4, dv_scale,
-             (gin && real) ? 8u * (uint32_t)g + 4u * plane + 64u * half * rs : kOutOfRange);
+        dma16(dscales, sbuf + lrow * 16, dv_scale, (gin && real) ? 8u * (uint32_t)g + 64u * half * rs : kOutOfRange);
       }
     }
   };
@@ -202,14 +205,17 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
   const uint32_t a_row = 128 * wm + r, b_row = BM + (BN / 2) * wn + r;
   u32x4 codes[2][NF];
   int sc[2][NF];
-  auto read_stage = [&](int cb, const uint8_t *gb, int sp) {
+  // stage sp of group g (LDS buffer gb): codes, and scale byte 8 (g & 1) + c
+  // of the row in the pair buffer
+  auto read_stage = [&](int cb, const uint8_t *gb, int g, int sp) {
     const int c = 2 * sp + h;
     const uint32_t slot = (uint32_t)((c ^ (r & 7)) * 16);
+    const uint8_t *sb = smem + 2 * kGroupBytes + ((g >> 1) & 1) * kScalePair + 8 * (g & 1) + c;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const uint32_t row = f < 4 ? a_row + 32 * f : b_row + 32 * (f - 4);
       codes[cb][f] = *reinterpret_cast<const u32x4 *>(gb + row * 128 + slot);
-      sc[cb][f] = gb[kCodeBytes + (c >> 2) * kScalePlane + row * 4 + (c & 3)];
+      sc[cb][f] = sb[row * 16];
     }
   };
 
@@ -226,7 +232,7 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
   dma_part(1, 1, 3);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  read_stage(0, smem, 0);
+  read_stage(0, smem, 0, 0);
   __builtin_amdgcn_s_waitcnt(0);
 
   // Stage s = 4g + P: read the next stage's operands (in the last stage of a
@@ -241,10 +247,10 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
     if (P == 3) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA of group g+1
       __syncthreads();
-      read_stage(nxt, gn, 0);
+      read_stage(nxt, gn, g + 1, 0);
       dma_part(g + 2, g & 1, 3);
     } else {
-      read_stage(nxt, gb, P + 1);
+      read_stage(nxt, gb, g, P + 1);
       dma_part(g + 1, (g + 1) & 1, P);
     }
 #pragma unroll
@@ -297,7 +303,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 k_mx_gemm(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const uint8_t *__restrict__ B,
           const uint8_t *__restrict__ SB, int64_t M, int64_t N, int64_t K, void *__restrict__ C, int64_t ldc,
           int n_big, int64_t n1) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kGroupBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
   const int pid = blockIdx.x;
   if (pid < n_big) {
     mx_gemm_tile<OUT_BF16, 256>(smem, pid, A, SA, B, SB, M, n1, K, C, ldc);
