@@ -205,18 +205,30 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
   const uint32_t a_row = 128 * wm + r, b_row = BM + (BN / 2) * wn + r;
   u32x4 codes[2][NF];
   int sc[2][NF];
-  // stage sp of group g (LDS buffer gb): codes, and scale byte 8 (g & 1) + c
-  // of the row in the pair buffer
-  auto read_stage = [&](int cb, const uint8_t *gb, int g, int sp) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 srow[NF];          // the fragment rows' 8 scale bytes of one group
+  auto read_stage = [&](int cb, const uint8_t *gb, int sp) {
     const int c = 2 * sp + h;
     const uint32_t slot = (uint32_t)((c ^ (r & 7)) * 16);
-    const uint8_t *sb = smem + 2 * kGroupBytes + ((g >> 1) & 1) * kScalePair + 8 * (g & 1) + c;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const uint32_t row = f < 4 ? a_row + 32 * f : b_row + 32 * (f - 4);
       codes[cb][f] = *reinterpret_cast<const u32x4 *>(gb + row * 128 + slot);
-      sc[cb][f] = sb[row * 16];
     }
+  };
+  // one 8-byte read per fragment row and group (a byte read per fragment
+  // and stage cost 10 % of the dgrad shape in a timing copy)
+  auto read_scales = [&](int g) {
+    const uint8_t *sb = smem + 2 * kGroupBytes + ((g >> 1) & 1) * kScalePair + 8 * (g & 1);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint32_t row = f < 4 ? a_row + 32 * f : b_row + 32 * (f - 4);
+      srow[f] = *reinterpret_cast<const u32x2 *>(sb + row * 16);
+    }
+  };
+  // fragment f's scale byte for stage sp: byte 2 sp + h of the group's 8
+  auto pick_scale = [&](int cb, int f, int sp) {
+    sc[cb][f] = (int)((srow[f][sp >> 1] >> (8 * ((2 * sp + h) & 3))) & 0xFFu);
   };
 
   float16_t acc[4][NB];
@@ -232,7 +244,10 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
   dma_part(1, 1, 3);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  read_stage(0, smem, 0, 0);
+  read_stage(0, smem, 0);
+  read_scales(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) pick_scale(0, f, 0);
   __builtin_amdgcn_s_waitcnt(0);
 
   // Stage s = 4g + P: read the next stage's operands (in the last stage of a
@@ -247,12 +262,15 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
     if (P == 3) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA of group g+1
       __syncthreads();
-      read_stage(nxt, gn, g + 1, 0);
+      read_stage(nxt, gn, 0);
+      read_scales(g + 1);
       dma_part(g + 2, g & 1, 3);
     } else {
-      read_stage(nxt, gb, g, P + 1);
+      read_stage(nxt, gb, P + 1);
       dma_part(g + 1, (g + 1) & 1, P);
     }
+    // the next stage's scale bytes are taken from srow between the MFMAs
+    constexpr int psp = P == 3 ? 0 : P + 1;
 #pragma unroll
     for (int u = 0; u < 4 * NB; ++u) {
       const int mi = u / NB, mj = (mi & 1) ? NB - 1 - u % NB : u % NB;
@@ -261,6 +279,10 @@ __device__ __forceinline__ void mx_gemm_tile(uint8_t *smem, int pid, const uint8
       const v8i bv = {(int)cbv.x, (int)cbv.y, (int)cbv.z, (int)cbv.w, 0, 0, 0, 0};
       acc[mi][mj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[mi][mj], 4, 4, 0, sc[cur][mi], 0,
                                                                    sc[cur][4 + mj]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = (u * NF) / (4 * NB); f < ((u + 1) * NF) / (4 * NB); ++f) pick_scale(nxt, f, psp);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   using P0 = std::integral_constant<int, 0>;
