@@ -222,18 +222,28 @@ __device__ __forceinline__ void mx8_gemm_tile(uint8_t *smem, int pid, const uint
   const uint32_t a_row = 128 * wm + r, b_row = BM + (BN / 2) * wn + r;
   u32x4 lo[2][NF], hi[2][NF];
   int sc[2][NF];
-  auto read_stage = [&](int cb, const uint8_t *gb, int g, int sp) {
+  uint32_t srow[NF];       // the fragment rows' 4 scale bytes of one group
+  auto read_stage = [&](int cb, const uint8_t *gb, int sp) {
     const int c0 = 4 * sp + h, c1 = 4 * sp + 2 + h;
-    // scale byte 4 (g % 4) + 2 sp + h of the row in the quad buffer of group g
-    const uint8_t *sb = smem + 2 * kGroupBytes + ((g >> 2) & 1) * kScaleQuad + 4 * (g & 3) + 2 * sp + h;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const uint32_t row = f < 4 ? a_row + 32 * f : b_row + 32 * (f - 4);
       lo[cb][f] = *reinterpret_cast<const u32x4 *>(gb + row * 128 + (uint32_t)((c0 ^ (r & 7)) * 16));
       hi[cb][f] = *reinterpret_cast<const u32x4 *>(gb + row * 128 + (uint32_t)((c1 ^ (r & 7)) * 16));
-      sc[cb][f] = sb[row * 16];
     }
   };
+  // one 4-byte read per fragment row and group (bytes 4 (g % 4) .. of the
+  // row in the quad buffer), instead of a byte read per fragment and stage
+  auto read_scales = [&](int g) {
+    const uint8_t *sb = smem + 2 * kGroupBytes + ((g >> 2) & 1) * kScaleQuad + 4 * (g & 3);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint32_t row = f < 4 ? a_row + 32 * f : b_row + 32 * (f - 4);
+      srow[f] = *reinterpret_cast<const uint32_t *>(sb + row * 16);
+    }
+  };
+  // fragment f's scale byte for stage sp: byte 2 sp + h of the group's 4
+  auto pick_scale = [&](int cb, int f, int sp) { sc[cb][f] = (int)((srow[f] >> (8 * (2 * sp + h))) & 0xFFu); };
 
   float16_t acc[4][NB];
 #pragma unroll
@@ -249,7 +259,10 @@ __device__ __forceinline__ void mx8_gemm_tile(uint8_t *smem, int pid, const uint
   dma_part(1, 1, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  read_stage(0, smem, 0, 0);
+  read_stage(0, smem, 0);
+  read_scales(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) pick_scale(0, f, 0);
   __builtin_amdgcn_s_waitcnt(0);
 
   // Stage s = 2g + P: read the next stage's operands (in the last stage of
@@ -267,13 +280,16 @@ __device__ __forceinline__ void mx8_gemm_tile(uint8_t *smem, int pid, const uint
     if (P == 1) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA of group g+1
       __syncthreads();
-      read_stage(nxt, gn, g + 1, 0);
+      read_stage(nxt, gn, 0);
+      read_scales(g + 1);
       dma_part(g + 2, g & 1, 0);
       dma_part(g + 2, g & 1, 1);
     } else {
-      read_stage(nxt, gb, g, 1);
+      read_stage(nxt, gb, 1);
       dma_part(g + 1, (g + 1) & 1, 2);
     }
+    // the next stage's scale bytes are taken from srow between the MFMAs
+    constexpr int psp = P == 1 ? 0 : 1;
 #pragma unroll
     for (int u = 0; u < 4 * NB; ++u) {
       const int mi = u / NB, mj = (mi & 1) ? NB - 1 - u % NB : u % NB;
@@ -282,6 +298,10 @@ __device__ __forceinline__ void mx8_gemm_tile(uint8_t *smem, int pid, const uint
       const v8i bv = {(int)bl.x, (int)bl.y, (int)bl.z, (int)bl.w, (int)bh.x, (int)bh.y, (int)bh.z, (int)bh.w};
       acc[mi][mj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[mi][mj], 0, 0, 0, sc[cur][mi], 0,
                                                                    sc[cur][4 + mj]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = (u * NF) / (4 * NB); f < ((u + 1) * NF) / (4 * NB); ++f) pick_scale(nxt, f, psp);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   using P0 = std::integral_constant<int, 0>;
