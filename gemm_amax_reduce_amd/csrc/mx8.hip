@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(kQT) k_mx8_quant_cols(const T *x, int64_t rows
   if (fast) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const uint32_t wd = *reinterpret_cast<const uint32_t *>(p + j * cols);
+      const uint32_t wd = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p + j * cols));
       if constexpr (CPT == 2) {
         y[0][j] = bf16_lo(wd);
         y[1][j] = bf16_hi(wd);
