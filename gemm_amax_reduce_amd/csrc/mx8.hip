@@ -98,9 +98,54 @@ template <typename T>
 __global__ void __launch_bounds__(kQT) k_mx8_quant_cols(const T *x, int64_t rows, int64_t cols, uint4 *codes,
                                                        uint8_t *scales) {
   constexpr int CPT = 4 / (int)sizeof(T);
+  constexpr int kCols = 64 * CPT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * CPT;
   const int64_t nkb = rows / 32, kb = (int64_t)blockIdx.y * 4 + wave;
+  // A workgroup tile wholly inside x (its kCols columns x 4 blocks, output
+  // lines 128-byte aligned) goes out through LDS as whole lines, 8 per store
+  // instruction, instead of two 16-byte pieces per lane and line.
+  const int64_t c_wg = (int64_t)blockIdx.x * kCols, kb_wg = (int64_t)blockIdx.y * 4;
+  const bool whole = (c_wg + kCols <= cols) && (kb_wg + 4 <= nkb) && (nkb % 4 == 0) && (CPT == 1 || cols % 2 == 0) &&
+                     ((uintptr_t)codes & 127) == 0 && ((uintptr_t)scales & 3) == 0;
+  __shared__ __attribute__((aligned(16))) uint4 tile_codes[kCols][9];    // 144-byte rows: no bank conflicts
+  __shared__ __attribute__((aligned(4))) uint8_t tile_scales[kCols][4];
+  if (whole) {
+    float y[CPT][32];
+    const T *p = x + 32 * kb * cols + c;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t wd = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p + j * cols));
+      if constexpr (CPT == 2) {
+        y[0][j] = bf16_lo(wd);
+        y[1][j] = bf16_hi(wd);
+      } else {
+        y[0][j] = __uint_as_float(wd);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      uint32_t w[8];
+      uint8_t sb;
+      mx8_encode32(y[e], w, &sb);
+      tile_codes[lane * CPT + e][2 * wave] = make_uint4(w[0], w[1], w[2], w[3]);
+      tile_codes[lane * CPT + e][2 * wave + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+      tile_scales[lane * CPT + e][wave] = sb;
+    }
+    __syncthreads();
+    // codes: column q / 8, 16-byte piece q % 8 of its line
+#pragma unroll
+    for (int r = 0; r < kCols * 8 / kQT; ++r) {
+      const int q = r * kQT + (int)threadIdx.x, col = q >> 3, piece = q & 7;
+      codes[2 * ((c_wg + col) * nkb + kb_wg) + piece] = tile_codes[col][piece];
+    }
+    if (threadIdx.x < kCols) {
+      const int col = threadIdx.x;
+      *reinterpret_cast<uint32_t *>(scales + (c_wg + col) * nkb + kb_wg) =
+          *reinterpret_cast<const uint32_t *>(tile_scales[col]);
+    }
+    return;
+  }
   if (c >= cols || kb >= nkb) return;
   const bool fast = (c + CPT <= cols) && (CPT == 1 || (cols % 2) == 0);
   float y[CPT][32];
