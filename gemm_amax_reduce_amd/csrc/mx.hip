@@ -29,7 +29,6 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kQT = kQuantThreads;
-typedef unsigned nt_u4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------ quantize ----
 
@@ -71,10 +70,10 @@ __global__ void __launch_bounds__(kQT) k_mx_quant_rows(const T *x, int64_t nbloc
     Load16<T>::run(x + 32 * b, y);
     Load16<T>::run(x + 32 * b + 16, y + 16);
     uint8_t s;
-    // streaming store: a wave writes 1 KB of whole code lines, written once
-    // (dY 8192 x 20480 bf16: 75.4 -> 72.1 us on one GPU)
-    const uint4 v = mx_encode32(y, &s);
-    __builtin_nontemporal_store((nt_u4){v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u4 *>(codes + b));
+    // ordinary stores: the codes stay in the last-level cache for the GEMM
+    // that reads them next (streaming stores made this call 3 us faster
+    // alone but the MXFP4 linear-layer step 0.4 % slower on one GPU)
+    codes[b] = mx_encode32(y, &s);
     scales[b] = s;
   }
 }

@@ -33,7 +33,6 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kQT = kQuantThreads;
-typedef unsigned nt_u4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------ quantize ----
 
@@ -76,13 +75,6 @@ __device__ __forceinline__ void mx8_encode32(const float *y, uint32_t *w, uint8_
 // out in two 16-byte stores).
 template <typename T>
 __global__ void __launch_bounds__(kQT) k_mx8_quant_rows(const T *x, int64_t nblocks, uint4 *codes, uint8_t *scales) {
-  // A wave whose 64 blocks all lie inside the tensor passes its 2 KB of
-  // codes through LDS, so each streaming store instruction writes one
-  // contiguous 1 KB run (a lane's own two 16-byte pieces leave 16-byte gaps
-  // in every instruction's span); the lanes of the last, partial wave store
-  // their own pieces.
-  __shared__ uint4 stage[kQT / 64][128];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t stride = (int64_t)gridDim.x * kQT;
   for (int64_t b = (int64_t)blockIdx.x * kQT + threadIdx.x; b < nblocks; b += stride) {
     float y[32];
@@ -91,26 +83,9 @@ __global__ void __launch_bounds__(kQT) k_mx8_quant_rows(const T *x, int64_t nblo
     uint32_t w[8];
     uint8_t s;
     mx8_encode32(y, w, &s);
+    codes[2 * b] = make_uint4(w[0], w[1], w[2], w[3]);
+    codes[2 * b + 1] = make_uint4(w[4], w[5], w[6], w[7]);
     scales[b] = s;
-    const int64_t base = b - lane;   // the wave's first block: uniform across the wave
-    if (base + 64 <= nblocks) {
-      stage[wave][2 * lane] = make_uint4(w[0], w[1], w[2], w[3]);
-      stage[wave][2 * lane + 1] = make_uint4(w[4], w[5], w[6], w[7]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const uint4 v0 = stage[wave][lane], v1 = stage[wave][64 + lane];
-      __builtin_nontemporal_store((nt_u4){v0.x, v0.y, v0.z, v0.w}, reinterpret_cast<nt_u4 *>(codes + 2 * base + lane));
-      __builtin_nontemporal_store((nt_u4){v1.x, v1.y, v1.z, v1.w},
-                                  reinterpret_cast<nt_u4 *>(codes + 2 * base + 64 + lane));
-      // every lane has read its pieces before the next pass overwrites them
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    } else {
-      codes[2 * b] = make_uint4(w[0], w[1], w[2], w[3]);
-      codes[2 * b + 1] = make_uint4(w[4], w[5], w[6], w[7]);
-    }
   }
 }
 
